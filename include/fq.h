@@ -1,0 +1,260 @@
+/*
+ * fq.h -- C ABI of the grouped-expert fake-quant library for AMD MI355X (gfx950).
+ *
+ * Scale-only quantisation-aware training of a MoE expert layer: the BF16 expert
+ * weights stay frozen, weights and every matmul input are fake-quantised
+ * (quantised, then dequantised) and only the quantiser scales receive
+ * gradients (AngelSlim "MCoreQAD Backend" page, opening paragraph; nxmr.cn
+ * article on the same backend, sections 一 and 二.3).  The experts of a layer
+ * are 3D-stacked, fake-quantised in one pass and multiplied by one grouped GEMM
+ * (nxmr.cn article, section 二.4).  The formats are those of the support matrix
+ * (AngelSlim page, Support Matrix; nxmr.cn article, section 三).
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" are HIP device pointers; "host" pointers are
+ *     read before the call returns.  The caller owns every buffer; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All device work is enqueued on it asynchronously; nothing is synchronised
+ *     and nothing is read back to the host.
+ *   - Every call returns an fq_status.  Arguments are validated on the host
+ *     before any HIP call; on a validation error nothing is launched.
+ *   - Gradients are overwritten, never accumulated.  Results are bitwise
+ *     deterministic for fixed inputs (no floating-point atomics).
+ *   - Device data are not checked: routing ids must lie in [0, E) and be
+ *     distinct per token, scales must be finite and > 0, inputs finite.
+ *     Violations give unspecified values (but no out-of-bounds access:
+ *     ids are range-checked by the kernels that index with them).
+ *   - bf16 tensors are row-major, 16-byte aligned; fp32 tensors 4-byte aligned.
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status --------------------------------------------------------------- */
+typedef enum {
+    FQ_OK = 0,
+    FQ_E_INVALID = -1,      /* null pointer, bad enum, inconsistent request    */
+    FQ_E_SHAPE = -2,        /* size negative or not divisible as required      */
+    FQ_E_UNSUPPORTED = -3,  /* valid descriptor this library does not implement */
+    FQ_E_WORKSPACE = -4,    /* workspace / saved buffer smaller than required  */
+    FQ_E_ALIGN = -5,        /* pointer not aligned as required                 */
+    FQ_E_HIP = -6           /* a HIP runtime call failed: see fq_last_hip_error */
+} fq_status;
+
+/* ---- quantiser descriptor ------------------------------------------------- */
+typedef enum {
+    FQ_NONE = 0,       /* quantiser disabled: identity (the BF16 teacher path)   */
+    FQ_NVFP4 = 1,      /* E2M1 elements, E4M3 block factor per 16, fp32 tensor scale */
+    FQ_INT = 2,        /* two's-complement integer grid [qmin, qmax]              */
+    FQ_FP8E4M3 = 3     /* OCP E4M3FN (max 448, saturating)                        */
+} fq_kind;
+
+typedef enum {
+    FQ_PER_TENSOR = 0, /* one scale per matrix (per batch entry / per expert)    */
+    FQ_PER_ROW = 1,    /* one scale per row: output channel (W) or token (A)     */
+    FQ_PER_GROUP = 2   /* one scale per `group` consecutive elements of a row    */
+} fq_gran;
+
+typedef enum {
+    FQ_LEARNABLE = 0,  /* scale is a trainable input; its gradient can be formed */
+    FQ_STATIC = 1,     /* calibrated scale, no gradient                          */
+    FQ_DYNAMIC = 2     /* scale = amax / max-code computed on the fly, detached  */
+} fq_source;
+
+typedef struct {
+    int32_t kind;      /* fq_kind                                                */
+    int32_t gran;      /* fq_gran                                                */
+    int32_t group;     /* FQ_PER_GROUP: elements per scale (16 for NVFP4)        */
+    int32_t source;    /* fq_source                                              */
+    int32_t qmin;      /* FQ_INT only: e.g. -8 / 7 (INT4), -128 / 127 (INT8)     */
+    int32_t qmax;
+} fq_qdesc;
+
+/*
+ * Numbers of one quantiser (every step is one IEEE fp32 operation):
+ *   effective scale s^ per element:
+ *     NVFP4, learnable/static:  d = E4M3(s_b / t), s^ = t * d   (s_b per 16-block, t per matrix)
+ *     NVFP4, dynamic:           d = E4M3(amax_16 / (6 t)), s^ = t * d   (t learnable)
+ *     INT/FP8, learnable/static: s^ = scale[tensor | row | group]
+ *     INT/FP8, dynamic:          s^ = amax(row | group) / (qmax | 448)
+ *   r = x / s^ (correctly rounded), q = nearest grid value of clamp(r), ties to
+ *   the even code, y = bf16_rne(q * s^).  s^ == 0 gives q = +-0, y = +-0.
+ *   Straight-through backward: dL/dx = g * [qmin <= r <= qmax] (learnable, static)
+ *   or g (dynamic); dL/ds = sum g * c, c = q - r inside, qmin/qmax outside;
+ *   for NVFP4 the learnable tensor scale of a dynamic quantiser gets sum g * c * d.
+ * Codes: NVFP4 nibble = sign(x) << 3 | E2M1 magnitude code; INT two's complement;
+ * FP8 byte = sign(x) << 7 | E4M3 magnitude code.  4-bit codes pack two per byte,
+ * the even column in the low nibble.  NVFP4 block-scale code = E4M3 byte of d.
+ */
+
+/* ---- format presets (the six names of the support matrix) ----------------- */
+typedef enum {
+    FQ_FMT_NVFP4 = 0,     /* W: NVFP4 learnable block scales; A: NVFP4 dynamic blocks, learnable tensor scale */
+    FQ_FMT_NVFP4A16 = 1,  /* W: NVFP4; A: bf16                                   */
+    FQ_FMT_W4A16 = 2,     /* W: INT4 [-8,7] learnable per group of 128; A: bf16  */
+    FQ_FMT_W8A8 = 3,      /* W: INT8 learnable per output channel; A: INT8 dynamic per token */
+    FQ_FMT_FP8 = 4,       /* W: FP8 learnable per output channel; A: FP8 dynamic per token */
+    FQ_FMT_W4AFP8 = 5     /* W: INT4 per group of 128; A: FP8 learnable per-expert tensor scale */
+} fq_format;
+
+/* Fill the four quantiser descriptors (host pointers) of a format.
+ * Errors: FQ_E_INVALID for a null pointer or an unknown format. */
+int fq_preset(int32_t format, fq_qdesc* w1, fq_qdesc* w2, fq_qdesc* a1, fq_qdesc* a2);
+
+/* ---- one tensor ----------------------------------------------------------- */
+/*
+ * Fake-quantise x [batch, rows, cols] along cols (the weight parametrisation
+ * and activation pre-hook of the nxmr.cn article, section 二.3, applied to a
+ * whole 3D stack at once, section 二.4), and optionally run the
+ * straight-through backward.
+ *
+ *   q            host; the quantiser.  FQ_NONE copies x.
+ *   x            device bf16 [batch, rows, cols]; cols % 8 == 0, 16-B aligned.
+ *   scale        device fp32: [batch] (per tensor), [batch, rows] (per row),
+ *                [batch, rows, cols/group] (per group; NVFP4: the block scale s_b).
+ *                NULL for dynamic sources.
+ *   tensor_scale device fp32 [batch]: NVFP4 only (static t for learnable/static
+ *                block scales; the learnable t of a dynamic quantiser).
+ *   y            device bf16, same shape as x (may alias x); NULL to skip.
+ *   codes        device u8, NULL to skip: 4-bit formats [batch, rows, cols/2]
+ *                (4-B aligned), 8-bit formats [batch, rows, cols] (8-B aligned).
+ *   block_codes  device u8 [batch, rows, cols/16], NVFP4 only; NULL to skip.
+ *   grad_y       device dL/dy, bf16 (grad_y_is_fp32 == 0) or fp32, shape of x;
+ *                NULL runs the forward only.
+ *   grad_x       device bf16 dL/dx (straight-through mask), NULL to skip; needs grad_y.
+ *   grad_scale   device fp32 dL/d(parameter), overwritten, NULL to skip; needs
+ *                grad_y and a quantiser with a trainable parameter: shape of
+ *                `scale` for learnable sources, [batch] for NVFP4 dynamic.
+ *   workspace    device scratch of fq_tensor_workspace_size() bytes (may be 0).
+ * Errors: FQ_E_INVALID, FQ_E_SHAPE (negative sizes, cols % 8, cols % group),
+ * FQ_E_UNSUPPORTED (dynamic per-tensor scales), FQ_E_ALIGN, FQ_E_WORKSPACE, FQ_E_HIP.
+ * A zero batch, rows or cols is a no-op.
+ */
+int fq_tensor(const fq_qdesc* q, int64_t batch, int64_t rows, int64_t cols,
+              const void* x, const float* scale, const float* tensor_scale,
+              void* y, uint8_t* codes, uint8_t* block_codes,
+              const void* grad_y, int32_t grad_y_is_fp32,
+              void* grad_x, float* grad_scale,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fq_tensor needs for these sizes (0 if none); 0 on bad input. */
+size_t fq_tensor_workspace_size(const fq_qdesc* q, int64_t batch, int64_t rows, int64_t cols);
+
+/* ---- the grouped SwiGLU expert layer -------------------------------------- */
+/*
+ * Per routed copy of token t in slot j, expert e = topk_ids[t, j]:
+ *   x^  = fq_a1,e(x[t])                       (activation quantiser of expert e)
+ *   z1  = bf16(x^ W1^[e]^T), g = z1[:I], u = z1[I:]
+ *   h   = bf16(silu(g) * u), h^ = fq_a2,e(h)
+ *   y_r = bf16(h^ W2^[e]^T)
+ *   y[t] = bf16(sum_j topk_w[t, j] * y_r)     (fp32, ascending j)
+ * with W^ = fq_w(W) over the whole 3D stack.  The router is not quantised:
+ * topk_ids / topk_w are inputs (nxmr.cn article, section 二.3).  A quantiser
+ * with kind FQ_NONE is the identity, so all-FQ_NONE is the BF16 teacher forward
+ * (AngelSlim page, opening paragraph).
+ * silu(g) = g / (1 + 2^(-g log2 e)) with 2^y evaluated as 2^rint(y) times the
+ * degree-7 Taylor polynomial of 2^f, f = y - rint(y), each step one fp32
+ * operation without fusion.
+ */
+typedef struct {
+    int64_t E;        /* experts, 1..1024                                        */
+    int64_t H;        /* hidden size, multiple of 128                             */
+    int64_t I;        /* expert intermediate size, multiple of 128                */
+    int64_t T;        /* tokens, >= 0                                             */
+    int64_t topk;     /* routed experts per token, 1..min(E, 64)                  */
+    fq_qdesc w1, w2;  /* weight quantisers of fc1 (gate|up) and fc2 (down)        */
+    fq_qdesc a1, a2;  /* input quantisers of fc1 and fc2 (per expert):
+                         FQ_NONE, NVFP4 dynamic, INT/FP8 per-row dynamic, or
+                         INT/FP8 per-tensor learnable/static                       */
+} fq_layer_desc;
+
+typedef struct {
+    const void* w1;     /* device bf16 [E, 2I, H], frozen; rows [0,I) gate, [I,2I) up */
+    const void* w2;     /* device bf16 [E, H, I], frozen                               */
+    const float* s_w1;  /* device fp32 scale of fc1's weight quantiser (fq_tensor layout, batch = E) */
+    const float* t_w1;  /* device fp32 [E] NVFP4 tensor scale of W1, else NULL        */
+    const float* s_w2;
+    const float* t_w2;
+    const float* s_a1;  /* device fp32 [E]: NVFP4 tensor scale or INT/FP8 per-tensor scale; NULL if dynamic per token */
+    const float* s_a2;
+} fq_expert_params;
+
+typedef struct {        /* device fp32, same shapes as the parameters; NULL to skip */
+    float* ds_w1;
+    float* ds_w2;
+    float* ds_a1;
+    float* ds_a2;
+} fq_expert_grads;
+
+/* Bytes of the buffer the forward fills for the backward, and of the scratch
+ * workspace of each call (0 on an invalid descriptor). */
+size_t fq_grouped_expert_saved_size(const fq_layer_desc* L);
+size_t fq_grouped_expert_workspace_size(const fq_layer_desc* L);
+
+/*
+ * Forward.  x device bf16 [T, H]; topk_ids device int32 [T, topk]; topk_w
+ * device fp32 [T, topk]; y device bf16 [T, H] (these may be NULL when T == 0).  `saved` (>= saved_size bytes,
+ * 256-B aligned) receives the routing, W^, x^, z1, h^ and y_r for the backward.
+ * Errors: FQ_E_INVALID, FQ_E_SHAPE, FQ_E_UNSUPPORTED, FQ_E_ALIGN,
+ * FQ_E_WORKSPACE, FQ_E_HIP.
+ */
+int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P,
+                          const void* x, const int32_t* topk_ids, const float* topk_w,
+                          void* y, void* saved, size_t saved_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Straight-through backward from dy (device bf16 [T, H]) and the forward's
+ * `saved` buffer (same x, ids, weights and parameters as the forward).
+ *   dx        device bf16 [T, H] dL/dx, NULL to skip.
+ *   d_topk_w  device fp32 [T, topk] dL/dtopk_w, NULL to skip.
+ *   G         host struct of device gradient pointers; each NULL to skip; a
+ *             non-NULL pointer for a quantiser without a trainable parameter
+ *             is FQ_E_INVALID.
+ * The frozen weights get no gradient (AngelSlim page, opening paragraph).
+ */
+int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P,
+                          const void* x, const int32_t* topk_ids, const float* topk_w,
+                          const void* dy, const void* saved, size_t saved_bytes,
+                          void* dx, float* d_topk_w, const fq_expert_grads* G,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Location of an intermediate inside `saved` (FQ_BUF_* < 100) or the backward's
+ * workspace (>= 100), for inspection between calls: *offset and *bytes.
+ * Errors: FQ_E_INVALID for an unknown id or an invalid descriptor. */
+typedef enum {
+    FQ_BUF_COUNTS = 0,   /* int32 [E] rows per expert                         */
+    FQ_BUF_OFFSETS = 1,  /* int32 [E+1] exclusive prefix sum of counts        */
+    FQ_BUF_ROW_OF = 2,   /* int32 [T*topk] routed row of flat index t*topk+j  */
+    FQ_BUF_SRC_OF = 3,   /* int32 [T*topk] flat index held by routed row r    */
+    FQ_BUF_W1HAT = 4,    /* bf16 [E, 2I, H]                                    */
+    FQ_BUF_W2HAT = 5,    /* bf16 [E, H, I]                                     */
+    FQ_BUF_XHAT = 6,     /* bf16 [T*topk, H] routed rows, experts ascending    */
+    FQ_BUF_Z1 = 7,       /* bf16 [T*topk, 2I]                                  */
+    FQ_BUF_HHAT = 8,     /* bf16 [T*topk, I]                                   */
+    FQ_BUF_YR = 9,       /* bf16 [T*topk, H]                                   */
+    FQ_BUF_DYR = 100,    /* bf16 [T*topk, H]  w * dY, permuted                 */
+    FQ_BUF_DHHAT = 101,  /* bf16 [T*topk, I]                                   */
+    FQ_BUF_DZ1 = 102,    /* bf16 [T*topk, 2I]                                  */
+    FQ_BUF_DXHAT = 103,  /* bf16 [T*topk, H]                                   */
+    FQ_BUF_DW1HAT = 104, /* fp32 [E, 2I, H]                                    */
+    FQ_BUF_DW2HAT = 105  /* fp32 [E, H, I]                                     */
+} fq_buffer;
+int fq_grouped_expert_buffer(const fq_layer_desc* L, int32_t which, size_t* offset, size_t* bytes);
+
+/* ---- diagnostics ----------------------------------------------------------- */
+const char* fq_status_string(int32_t status);   /* static string                */
+const char* fq_last_hip_error(void);            /* thread-local; after FQ_E_HIP */
+int32_t fq_abi_version(void);                   /* 1                            */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FQ_H */

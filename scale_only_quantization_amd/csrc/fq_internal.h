@@ -1,0 +1,160 @@
+// Internal launch interface between the C ABI (fq_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fq {
+
+// One quantiser, resolved on the host.
+struct QParams {
+    int kind, gran, group, source;
+    float qmin, qmax;      // grid bounds (NVFP4 +-6, FP8 +-448, INT [qmin, qmax])
+    float qdiv;            // dynamic INT/FP8: amax divisor (qmax or 448)
+};
+
+// fq_tensor over [batch, rows, cols].
+struct TensorArgs {
+    QParams q;
+    int64_t batch, rows, cols;
+    const uint16_t* x;
+    const float* scale;
+    const float* tscale;
+    uint16_t* y;
+    uint8_t* codes;
+    uint8_t* bcodes;
+    const void* gy;
+    int gy_fp32;
+    uint16_t* gx;
+    float* gscale;
+    float* rowpart;        // workspace [batch * rows] (per-tensor gradients)
+};
+
+hipError_t launch_tensor_fwd(const TensorArgs& a, hipStream_t st);
+hipError_t launch_tensor_bwd(const TensorArgs& a, hipStream_t st);
+size_t tensor_workspace_bytes(const QParams& q, int64_t batch, int64_t rows);
+
+// ------------------------------------------------------------------ layer ---
+constexpr int GEMM_BM = 128;          // routed rows per GEMM tile (tile table granularity)
+
+struct RouteArgs {
+    const int32_t* ids;    // [R]
+    int64_t R;
+    int E;
+    int32_t* counts;       // [E]
+    int32_t* offsets;      // [E+1]
+    int32_t* row_of;       // [R]
+    int32_t* src_of;       // [R]
+    int32_t* tile_expert;  // [max_tiles]
+    int32_t* tile_row0;    // [max_tiles]
+    int32_t* num_tiles;    // [1]
+    int32_t* order;        // [E] experts by descending count
+    int32_t* hist;         // workspace [nblk, E]
+    int32_t* local_rank;   // workspace [R]
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+int64_t route_blocks(int64_t R);
+int64_t max_mtiles(int64_t R, int E);
+
+// Activation quantiser of the layer (per expert parameter vector or none).
+struct ActQ {
+    QParams q;
+    const float* s;        // [E] per-expert scale (NVFP4 tensor scale / INT-FP8 per-tensor), or null
+};
+
+struct PermuteArgs {       // x [T,H] -> xhat rows (fq_a1 per expert)
+    const uint16_t* x;
+    const int32_t* ids;
+    const int32_t* row_of;
+    uint16_t* xhat;
+    int64_t T;
+    int k, H, E;
+    ActQ a1;
+};
+hipError_t launch_permute_a1(const PermuteArgs& a, hipStream_t st);
+
+struct SwigluArgs {        // z1 [R, 2I] -> hhat [R, I] (fq_a2 per expert)
+    const uint16_t* z1;
+    const int32_t* ids;
+    const int32_t* src_of;
+    uint16_t* hhat;
+    int64_t R;
+    int I, E;
+    ActQ a2;
+};
+hipError_t launch_swiglu_a2(const SwigluArgs& a, hipStream_t st);
+
+struct CombineArgs {       // y[t] = sum_j w y_r[row_of]
+    const uint16_t* yr;
+    const int32_t* row_of;
+    const float* w;
+    uint16_t* y;
+    int64_t T;
+    int k, H;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+struct PermuteDyArgs {     // dY_r[row] = w dY[t]; dw = <dY[t], Y_r[row]>
+    const uint16_t* dy;
+    const float* w;
+    const int32_t* row_of;
+    const uint16_t* yr;
+    uint16_t* dyr;
+    float* dw;
+    int64_t T;
+    int k, H;
+};
+hipError_t launch_permute_dy(const PermuteDyArgs& a, hipStream_t st);
+
+struct SwigluBwdArgs {     // (z1, dhhat) -> dz1, per-row partial of ds_a2
+    const uint16_t* z1;
+    const uint16_t* dhh;
+    const int32_t* ids;
+    const int32_t* src_of;
+    uint16_t* dz1;
+    float* rowpart;        // [R] or null
+    int64_t R;
+    int I, E;
+    ActQ a2;
+};
+hipError_t launch_swiglu_bwd(const SwigluBwdArgs& a, hipStream_t st);
+
+struct UnpermuteArgs {     // dX[t] = sum_j mask * dXhat[row]; per-row partial of ds_a1
+    const uint16_t* x;
+    const uint16_t* dxh;
+    const int32_t* ids;
+    const int32_t* row_of;
+    uint16_t* dx;          // or null
+    float* rowpart;        // [R] or null
+    int64_t T;
+    int k, H, E;
+    ActQ a1;
+};
+hipError_t launch_unpermute_a1(const UnpermuteArgs& a, hipStream_t st);
+
+// ds[e] = sum of rowpart over rows [offsets[e], offsets[e+1]) in a fixed order
+hipError_t launch_segment_sum(const float* rowpart, const int32_t* offsets, int E,
+                              float* out, hipStream_t st);
+
+// ------------------------------------------------------------------ GEMMs ---
+// C = A B^T per expert over the routed rows (forward), A K-contiguous, B [N, K].
+struct GemmArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    void* C;
+    int64_t lda, ldb, ldc;
+    int64_t strideB, strideC;     // per-expert strides (elements)
+    int N, K;
+    int64_t R;
+    int E;
+    const int32_t* offsets;
+    const int32_t* tile_expert;
+    const int32_t* tile_row0;
+    const int32_t* num_tiles;
+    const int32_t* order;
+};
+hipError_t launch_gemm_fwd(const GemmArgs& g, hipStream_t st);    // B K-contiguous
+hipError_t launch_gemm_dgrad(const GemmArgs& g, hipStream_t st);  // B N-contiguous ([K, N])
+hipError_t launch_gemm_wgrad(const GemmArgs& g, hipStream_t st);  // C[e] fp32 [N, K] = A_e^T B_e
+
+}  // namespace fq

@@ -1,0 +1,682 @@
+// Routing and the element-wise stages of the grouped SwiGLU expert layer.
+//
+// The grouped-experts design of the nxmr.cn article on MCoreQAD (section 二.4)
+// gathers the routed copies of the tokens expert by expert so that one grouped
+// GEMM covers all experts; every matmul input is fake-quantised by its
+// expert's activation quantiser on the way (section 二.3), and the router's
+// ids and weights are unquantised inputs.
+//
+// Row order (a stable counting sort): experts ascending, and inside an expert
+// the flat routing index t*k + j ascending.  All reductions below use fixed
+// trees, so results are bitwise reproducible.
+#include "fq_common.h"
+#include "fq_internal.h"
+
+namespace fq {
+
+namespace {
+
+constexpr int TPB = 256;
+constexpr int RPB = TPB / WAVE;      // rows (tokens) per block, one per wave
+constexpr int RB = 1024;             // routing elements per block
+
+__device__ __forceinline__ int clamp_id(int id, int E) { return id < 0 ? 0 : (id >= E ? E - 1 : id); }
+// routed-row indices read back from the routing tables, kept in [0, R)
+__device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t R) { return r < 0 ? 0 : (r >= R ? R - 1 : r); }
+
+// ------------------------------------------------------------------ routing --
+// Per block of RB flat indices: histogram and the stable rank of each element
+// among equal ids inside the block.  Equal ids inside a 64-element wave slice
+// are found with one ballot per id bit; the wave slices of the block are
+// ordered by a per-wave running histogram in LDS.
+__global__ __launch_bounds__(TPB) void k_route_local(const int32_t* ids, int64_t R, int E,
+                                                     int nbits, int32_t* hist, int32_t* local_rank) {
+    extern __shared__ int32_t whist[];                    // [4][E]
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < 4 * E; i += TPB) whist[i] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * RB + w * 256;
+    int rk[4], idv[4];
+#pragma unroll
+    for (int sc = 0; sc < 4; ++sc) {
+        const int64_t i = base + sc * WAVE + lane;
+        const bool valid = i < R;
+        const int id = valid ? clamp_id(ids[i], E) : 0;
+        idv[sc] = id;
+        uint64_t m = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool on = (id >> bit) & 1;
+            const uint64_t bal = __ballot(valid && on);
+            m &= on ? bal : ~bal;
+        }
+        int before = 0;
+        if (valid) {
+            before = whist[w * E + id];
+            rk[sc] = before + __popcll(m & ((1ull << lane) - 1ull));
+        }
+        // all lanes of this wave read the running count before the group's
+        // lowest lane adds the group size (one instruction stream, in order)
+        if (valid && lane == __ffsll((unsigned long long)m) - 1) whist[w * E + id] = before + __popcll(m);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += TPB) {
+        const int s0 = whist[e], s1 = whist[E + e], s2 = whist[2 * E + e], s3 = whist[3 * E + e];
+        whist[e] = 0;
+        whist[E + e] = s0;
+        whist[2 * E + e] = s0 + s1;
+        whist[3 * E + e] = s0 + s1 + s2;
+        hist[(int64_t)blockIdx.x * E + e] = s0 + s1 + s2 + s3;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sc = 0; sc < 4; ++sc) {
+        const int64_t i = base + sc * WAVE + lane;
+        if (i < R) local_rank[i] = whist[w * E + idv[sc]] + rk[sc];
+    }
+}
+
+// One block: per-expert counts, block bases, offsets, the GEMM row-tile table
+// and the experts ordered by descending count (ties by id).
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, int E, int32_t* counts,
+                                                     int32_t* offsets, int32_t* tile_expert,
+                                                     int32_t* tile_row0, int32_t* num_tiles,
+                                                     int32_t* order) {
+    __shared__ int32_t s_cnt[1024];
+    __shared__ int32_t s_a[1024];
+    __shared__ int32_t s_b[1024];
+    const int e = threadIdx.x;
+    int running = 0;
+    if (e < E) {
+        for (int b = 0; b < nblk; ++b) {
+            const int h = hist[(int64_t)b * E + e];
+            hist[(int64_t)b * E + e] = running;
+            running += h;
+        }
+    }
+    const int cnt = e < E ? running : 0;
+    const int mt = (cnt + GEMM_BM - 1) / GEMM_BM;
+    s_cnt[e] = cnt;
+    s_a[e] = cnt;
+    s_b[e] = mt;
+    __syncthreads();
+    // inclusive Hillis-Steele scans of counts and of row tiles
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int va = e >= d ? s_a[e - d] : 0;
+        const int vb = e >= d ? s_b[e - d] : 0;
+        __syncthreads();
+        s_a[e] += va;
+        s_b[e] += vb;
+        __syncthreads();
+    }
+    const int off = s_a[e] - cnt;
+    const int tstart = s_b[e] - mt;
+    if (e < E) {
+        counts[e] = cnt;
+        offsets[e] = off;
+        if (e == E - 1) {
+            offsets[E] = off + cnt;
+            num_tiles[0] = tstart + mt;
+        }
+        for (int i = 0; i < mt; ++i) {
+            tile_expert[tstart + i] = e;
+            tile_row0[tstart + i] = off + i * GEMM_BM;
+        }
+        int rank = 0;
+        for (int o = 0; o < E; ++o) {
+            const int c = s_cnt[o];
+            rank += (c > cnt) || (c == cnt && o < e);
+        }
+        order[rank] = e;
+        for (int b = 0; b < nblk; ++b) hist[(int64_t)b * E + e] += off;
+    }
+}
+
+__global__ __launch_bounds__(TPB) void k_route_scatter(const int32_t* ids, int64_t R, int E,
+                                                       const int32_t* hist, const int32_t* local_rank,
+                                                       int32_t* row_of, int32_t* src_of) {
+    const int64_t i0 = (int64_t)blockIdx.x * RB;
+    for (int j = threadIdx.x; j < RB; j += TPB) {
+        const int64_t i = i0 + j;
+        if (i >= R) break;
+        const int id = clamp_id(ids[i], E);
+        const int row = hist[(int64_t)blockIdx.x * E + id] + local_rank[i];
+        row_of[i] = row;
+        if (row >= 0 && row < R) src_of[row] = (int32_t)i;
+    }
+}
+
+// --------------------------------------------------------------- activation --
+// Effective scale of an 8-element vector under the layer's activation
+// quantiser of expert e.  `bm` is the vector's 16-block amax (NVFP4), `gm`
+// its group amax (INT/FP8 per-group dynamic), `row_s` the dynamic per-row scale.
+template <int KIND>
+__device__ __forceinline__ float act_scale(const ActQ& a, int e, float bm, float gm, float row_s,
+                                           float* dfac) {
+    *dfac = 1.0f;
+    if (KIND == K_NVFP4) {
+        const float t = a.s[e];
+        const float d = e4m3_round(fminf(bm / (6.0f * t), 448.0f));
+        *dfac = d;
+        return t * d;
+    }
+    if (a.q.source != S_DYNAMIC) return a.s[e];          // per-expert per-tensor scale
+    if (a.q.gran == G_ROW) return row_s;
+    return gm / a.q.qdiv;
+}
+
+template <int KIND>
+__device__ __forceinline__ void quant8(const float* f, float s, float qmin, float qmax, float* y) {
+    Div dv;
+    dv.set(s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = quant_elem<KIND>(f[i], dv, qmin, qmax).q * s;
+}
+
+// straight-through terms of 8 elements: sum g*c, and the pass mask applied to g
+template <int KIND>
+__device__ __forceinline__ float ste8(const float* f, const float* g, float s, float qmin, float qmax,
+                                      bool dyn, float* gx) {
+    Div dv;
+    dv.set(s);
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const Elem el = quant_elem<KIND>(f[i], dv, qmin, qmax);
+        part = __builtin_fmaf(g[i], ste_c(el, qmin, qmax), part);
+        gx[i] = (dyn || el.inside) ? g[i] : 0.0f;
+    }
+    return part;
+}
+
+__device__ __forceinline__ float amax8(const float* f) {
+    float m = fabsf(f[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    return m;
+}
+
+// ------------------------------------------------------------ F2 permute+A1 --
+// One wave per token: x[t] is read once, block / row statistics formed once,
+// then each of its k routed copies is quantised with its expert's quantiser
+// and written to its row.
+template <int KIND, int NV>
+__global__ __launch_bounds__(TPB) void k_permute_a1(PermuteArgs a) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int nvec = a.H >> 3;
+    const float qmin = a.a1.q.qmin, qmax = a.a1.q.qmax;
+    const int gl = a.a1.q.group >> 3;
+    const bool indep = KIND != K_NONE && KIND != K_NVFP4 && a.a1.q.source == S_DYNAMIC;
+    for (int64_t t = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); t < a.T; t += (int64_t)gridDim.x * RPB) {
+        uint4 xv[NV];
+        float bm[NV];
+        float rm = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            const int v = lane + c * WAVE;
+            xv[c] = v < nvec ? reinterpret_cast<const uint4*>(a.x + t * a.H)[v] : make_uint4(0, 0, 0, 0);
+            float f[8];
+            unpack8(xv[c], f);
+            const float m = amax8(f);
+            rm = fmaxf(rm, m);
+            if (KIND == K_NVFP4) bm[c] = fmaxf(m, __shfl_xor(m, 1));
+            else if (KIND != K_NONE && a.a1.q.gran == G_GROUP) bm[c] = group_max(m, gl);
+            else bm[c] = 0.0f;
+        }
+        float row_s = 0.0f;
+        if (KIND != K_NONE && KIND != K_NVFP4 && a.a1.q.gran == G_ROW && a.a1.q.source == S_DYNAMIC)
+            row_s = wave_max(rm) / a.a1.q.qdiv;
+        uint4 qv[NV];
+        if (indep) {                                    // same quantised row for every expert
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                float f[8], y[8], dfac;
+                unpack8(xv[c], f);
+                quant8<KIND>(f, act_scale<KIND>(a.a1, 0, bm[c], bm[c], row_s, &dfac), qmin, qmax, y);
+                qv[c] = pack8(y);
+            }
+        }
+        for (int j = 0; j < a.k; ++j) {
+            const int64_t fi = t * a.k + j;
+            const int e = clamp_id(a.ids[fi], a.E);
+            const int64_t row = clamp_row(a.row_of[fi], a.T * a.k);
+            uint4* dst = reinterpret_cast<uint4*>(a.xhat + row * a.H);
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                const int v = lane + c * WAVE;
+                if (v >= nvec) continue;
+                if (KIND == K_NONE) {
+                    dst[v] = xv[c];
+                } else if (indep) {
+                    dst[v] = qv[c];
+                } else {
+                    float f[8], y[8], dfac;
+                    unpack8(xv[c], f);
+                    quant8<KIND>(f, act_scale<KIND>(a.a1, e, bm[c], bm[c], row_s, &dfac), qmin, qmax, y);
+                    dst[v] = pack8(y);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ SiLU ----
+// silu(g) = g / (1 + 2^y), y = -g log2(e): 2^y = 2^rint(y) * P(y - rint(y)),
+// P the degree-7 Taylor polynomial of 2^f (coefficients (ln 2)^i / i!, rounded
+// to fp32), Horner with separate multiply and add.
+__device__ __forceinline__ float exp2_taylor(float y) {
+    const float n = rintf(y);
+    const float f = y - n;
+    float p = 0x1.ffcbfcp-17f;
+    p = p * f; p = p + 0x1.430912p-13f;
+    p = p * f; p = p + 0x1.5d87fep-10f;
+    p = p * f; p = p + 0x1.3b2ab6p-7f;
+    p = p * f; p = p + 0x1.c6b08ep-5f;
+    p = p * f; p = p + 0x1.ebfbe0p-3f;
+    p = p * f; p = p + 0x1.62e430p-1f;
+    p = p * f; p = p + 1.0f;
+    return ldexpf(p, (int)n);
+}
+__device__ __forceinline__ float exp_neg(float g) {        // e^-g as the forward defines it
+    float y = (-g) * 0x1.715476p+0f;
+    y = fminf(fmaxf(y, -200.0f), 200.0f);
+    return exp2_taylor(y);
+}
+
+// ------------------------------------------------------------- F5 SwiGLU+A2 --
+template <int KIND, int NV>
+__global__ __launch_bounds__(TPB) void k_swiglu_a2(SwigluArgs a) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int nvec = a.I >> 3;
+    const float qmin = a.a2.q.qmin, qmax = a.a2.q.qmax;
+    const int gl = a.a2.q.group >> 3;
+    for (int64_t r = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); r < a.R; r += (int64_t)gridDim.x * RPB) {
+        const int e = clamp_id(a.ids[clamp_row(a.src_of[r], a.R)], a.E);
+        const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + r * 2 * (int64_t)a.I);
+        uint4 hv[NV];
+        float bm[NV];
+        float rm = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            const int v = lane + c * WAVE;
+            float h[8];
+            if (v < nvec) {
+                float g[8], u[8];
+                unpack8(zr[v], g);
+                unpack8(zr[v + nvec], u);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) h[i] = (g[i] / (1.0f + exp_neg(g[i]))) * u[i];
+                hv[c] = pack8(h);
+                unpack8(hv[c], h);                       // h as stored (bf16)
+            } else {
+                hv[c] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) h[i] = 0.0f;
+            }
+            const float m = amax8(h);
+            rm = fmaxf(rm, m);
+            if (KIND == K_NVFP4) bm[c] = fmaxf(m, __shfl_xor(m, 1));
+            else if (KIND != K_NONE && a.a2.q.gran == G_GROUP) bm[c] = group_max(m, gl);
+            else bm[c] = 0.0f;
+        }
+        float row_s = 0.0f;
+        if (KIND != K_NONE && KIND != K_NVFP4 && a.a2.q.gran == G_ROW && a.a2.q.source == S_DYNAMIC)
+            row_s = wave_max(rm) / a.a2.q.qdiv;
+        uint4* dst = reinterpret_cast<uint4*>(a.hhat + r * a.I);
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            const int v = lane + c * WAVE;
+            if (v >= nvec) continue;
+            if (KIND == K_NONE) {
+                dst[v] = hv[c];
+            } else {
+                float h[8], y[8], dfac;
+                unpack8(hv[c], h);
+                quant8<KIND>(h, act_scale<KIND>(a.a2, e, bm[c], bm[c], row_s, &dfac), qmin, qmax, y);
+                dst[v] = pack8(y);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- F7 combine ---
+template <int NV>
+__global__ __launch_bounds__(TPB) void k_combine(CombineArgs a) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int nvec = a.H >> 3;
+    for (int64_t t = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); t < a.T; t += (int64_t)gridDim.x * RPB) {
+        float acc[NV][8];
+#pragma unroll
+        for (int c = 0; c < NV; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
+        for (int j = 0; j < a.k; ++j) {
+            const int64_t fi = t * a.k + j;
+            const float w = a.w[fi];
+            const uint4* src = reinterpret_cast<const uint4*>(a.yr + clamp_row(a.row_of[fi], a.T * a.k) * a.H);
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                const int v = lane + c * WAVE;
+                if (v >= nvec) continue;
+                float f[8];
+                unpack8(src[v], f);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[c][i] = acc[c][i] + w * f[i];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            const int v = lane + c * WAVE;
+            if (v < nvec) reinterpret_cast<uint4*>(a.y + t * a.H)[v] = pack8(acc[c]);
+        }
+    }
+}
+
+// ------------------------------------------------------------- B1 permute dY --
+template <int NV>
+__global__ __launch_bounds__(TPB) void k_permute_dy(PermuteDyArgs a) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int nvec = a.H >> 3;
+    for (int64_t t = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); t < a.T; t += (int64_t)gridDim.x * RPB) {
+        float d[NV][8];
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            const int v = lane + c * WAVE;
+            if (v < nvec) unpack8(reinterpret_cast<const uint4*>(a.dy + t * a.H)[v], d[c]);
+            else
+#pragma unroll
+                for (int i = 0; i < 8; ++i) d[c][i] = 0.0f;
+        }
+        for (int j = 0; j < a.k; ++j) {
+            const int64_t fi = t * a.k + j;
+            const float w = a.w[fi];
+            const int64_t row = clamp_row(a.row_of[fi], a.T * a.k);
+            float part = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                const int v = lane + c * WAVE;
+                if (v >= nvec) continue;
+                float o[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = w * d[c][i];
+                reinterpret_cast<uint4*>(a.dyr + row * a.H)[v] = pack8(o);
+                if (a.dw) {
+                    float yv[8];
+                    unpack8(reinterpret_cast<const uint4*>(a.yr + row * a.H)[v], yv);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) part = __builtin_fmaf(d[c][i], yv[i], part);
+                }
+            }
+            if (a.dw) {
+                part = wave_sum(part);
+                if (lane == 0) a.dw[fi] = part;
+            }
+        }
+    }
+}
+
+// --------------------------------------------- B4 A2 backward + SwiGLU backward --
+template <int KIND>
+__global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int nvec = a.I >> 3;
+    const float qmin = a.a2.q.qmin, qmax = a.a2.q.qmax;
+    const bool dyn = a.a2.q.source == S_DYNAMIC;
+    // NVFP4 (dynamic blocks, learnable tensor scale) and per-tensor INT/FP8
+    // need the forward's codec terms; per-row/group dynamic quantisers pass
+    // the gradient straight and own no parameter.
+    const bool recompute = KIND == K_NVFP4 || (KIND != K_NONE && !dyn);
+    for (int64_t r = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); r < a.R; r += (int64_t)gridDim.x * RPB) {
+        const int e = clamp_id(a.ids[clamp_row(a.src_of[r], a.R)], a.E);
+        const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + r * 2 * (int64_t)a.I);
+        const uint4* dr = reinterpret_cast<const uint4*>(a.dhh + r * a.I);
+        uint4* out = reinterpret_cast<uint4*>(a.dz1 + r * 2 * (int64_t)a.I);
+        float part_row = 0.0f;
+        for (int v0 = 0; v0 < nvec; v0 += WAVE) {
+            const int v = v0 + lane;
+            const bool act = v < nvec;
+            float g[8], u[8], dh[8], sg[8], h[8];
+            if (act) {
+                unpack8(zr[v], g);
+                unpack8(zr[v + nvec], u);
+                unpack8(dr[v], dh);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { g[i] = 0.0f; u[i] = 0.0f; dh[i] = 0.0f; }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float den = 1.0f + exp_neg(g[i]);
+                sg[i] = 1.0f / den;                          // sigmoid(g)
+                h[i] = (g[i] / den) * u[i];
+            }
+            if (recompute) {
+                float hq[8];
+                unpack8(pack8(h), hq);                       // h as the forward stored it
+                float bm = 0.0f;
+                if (KIND == K_NVFP4) {
+                    const float m = amax8(hq);
+                    bm = fmaxf(m, __shfl_xor(m, 1));
+                }
+                float dfac;
+                const float s = act_scale<KIND>(a.a2, e, bm, bm, 0.0f, &dfac);
+                float gx[8];
+                const float part = ste8<KIND>(hq, dh, s, qmin, qmax, dyn, gx);
+                if (act) part_row = __builtin_fmaf(part, dfac, part_row);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dh[i] = gx[i];
+            }
+            if (act) {
+                float dg[8], du[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float s = sg[i];
+                    const float silu = g[i] * s;
+                    dg[i] = dh[i] * u[i] * (s * (1.0f + g[i] * (1.0f - s)));
+                    du[i] = dh[i] * silu;
+                }
+                out[v] = pack8(dg);
+                out[v + nvec] = pack8(du);
+            }
+        }
+        if (a.rowpart) {
+            const float tot = wave_sum(part_row);
+            if (lane == 0) a.rowpart[r] = tot;
+        }
+    }
+}
+
+// ------------------------------------------- B7 A1 backward + unpermute-sum --
+template <int KIND, int NV>
+__global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int nvec = a.H >> 3;
+    const float qmin = a.a1.q.qmin, qmax = a.a1.q.qmax;
+    const bool dyn = a.a1.q.source == S_DYNAMIC;
+    const bool recompute = KIND == K_NVFP4 || (KIND != K_NONE && !dyn);
+    for (int64_t t = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); t < a.T; t += (int64_t)gridDim.x * RPB) {
+        uint4 xv[NV];
+        float bm[NV];
+        if (recompute) {
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                const int v = lane + c * WAVE;
+                xv[c] = v < nvec ? reinterpret_cast<const uint4*>(a.x + t * a.H)[v] : make_uint4(0, 0, 0, 0);
+                float f[8];
+                unpack8(xv[c], f);
+                const float m = amax8(f);
+                bm[c] = KIND == K_NVFP4 ? fmaxf(m, __shfl_xor(m, 1)) : 0.0f;
+            }
+        }
+        float acc[NV][8];
+#pragma unroll
+        for (int c = 0; c < NV; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
+        for (int j = 0; j < a.k; ++j) {
+            const int64_t fi = t * a.k + j;
+            const int e = clamp_id(a.ids[fi], a.E);
+            const int64_t row = clamp_row(a.row_of[fi], a.T * a.k);
+            const uint4* src = reinterpret_cast<const uint4*>(a.dxh + row * a.H);
+            float part_row = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                const int v = lane + c * WAVE;
+                if (v >= nvec) continue;
+                float d[8];
+                unpack8(src[v], d);
+                if (recompute) {
+                    float f[8], gx[8], dfac;
+                    unpack8(xv[c], f);
+                    const float s = act_scale<KIND>(a.a1, e, bm[c], bm[c], 0.0f, &dfac);
+                    const float part = ste8<KIND>(f, d, s, qmin, qmax, dyn, gx);
+                    part_row = __builtin_fmaf(part, dfac, part_row);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[c][i] = acc[c][i] + gx[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[c][i] = acc[c][i] + d[i];
+                }
+            }
+            if (a.rowpart) {
+                const float tot = wave_sum(part_row);
+                if (lane == 0) a.rowpart[row] = tot;
+            }
+        }
+        if (a.dx) {
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                const int v = lane + c * WAVE;
+                if (v < nvec) reinterpret_cast<uint4*>(a.dx + t * a.H)[v] = pack8(acc[c]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------- per-expert segment sum --
+__global__ __launch_bounds__(TPB) void k_segment_sum(const float* rowpart, const int32_t* offsets, float* out) {
+    __shared__ float red[TPB];
+    const int e = blockIdx.x;
+    const int64_t lo = offsets[e], hi = offsets[e + 1];
+    float acc = 0.0f;
+    for (int64_t r = lo + threadIdx.x; r < hi; r += TPB) acc += rowpart[r];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = TPB / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[e] = red[0];
+}
+
+unsigned grid_waves(int64_t n) {
+    int64_t g = (n + RPB - 1) / RPB;
+    if (g < 1) g = 1;
+    if (g > (1 << 20)) g = 1 << 20;
+    return (unsigned)g;
+}
+
+int nv_for(int H) { return H <= 1024 ? 2 : H <= 2048 ? 4 : H <= 4096 ? 8 : 16; }
+
+}  // namespace
+
+int64_t route_blocks(int64_t R) { return (R + RB - 1) / RB; }
+int64_t max_mtiles(int64_t R, int E) { return (R + GEMM_BM - 1) / GEMM_BM + E; }
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+    if (a.E > 1024) return hipErrorInvalidValue;
+    const int64_t nblk = route_blocks(a.R);
+    int nbits = 0;
+    while ((1 << nbits) < a.E) ++nbits;
+    if (nblk > 0) {
+        hipLaunchKernelGGL(k_route_local, dim3((unsigned)nblk), dim3(TPB), 4 * a.E * sizeof(int32_t), st,
+                           a.ids, a.R, a.E, nbits, a.hist, a.local_rank);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, a.hist, (int)nblk, a.E, a.counts,
+                       a.offsets, a.tile_expert, a.tile_row0, a.num_tiles, a.order);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || nblk == 0) return err;
+    hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nblk), dim3(TPB), 0, st, a.ids, a.R, a.E, a.hist,
+                       a.local_rank, a.row_of, a.src_of);
+    return hipGetLastError();
+}
+
+#define FQ_NV_SWITCH(NVV, KERNEL, KIND, GRID, ARGS)                                         \
+    switch (NVV) {                                                                           \
+    case 2: hipLaunchKernelGGL((KERNEL<KIND, 2>), GRID, dim3(TPB), 0, st, ARGS); break;      \
+    case 4: hipLaunchKernelGGL((KERNEL<KIND, 4>), GRID, dim3(TPB), 0, st, ARGS); break;      \
+    case 8: hipLaunchKernelGGL((KERNEL<KIND, 8>), GRID, dim3(TPB), 0, st, ARGS); break;      \
+    default: hipLaunchKernelGGL((KERNEL<KIND, 16>), GRID, dim3(TPB), 0, st, ARGS); break;    \
+    }
+
+#define FQ_KIND_NV_SWITCH(KINDV, NVV, KERNEL, GRID, ARGS)                                   \
+    switch (KINDV) {                                                                         \
+    case K_NONE: FQ_NV_SWITCH(NVV, KERNEL, K_NONE, GRID, ARGS); break;                       \
+    case K_NVFP4: FQ_NV_SWITCH(NVV, KERNEL, K_NVFP4, GRID, ARGS); break;                     \
+    case K_INT: FQ_NV_SWITCH(NVV, KERNEL, K_INT, GRID, ARGS); break;                         \
+    default: FQ_NV_SWITCH(NVV, KERNEL, K_FP8, GRID, ARGS); break;                            \
+    }
+
+hipError_t launch_permute_a1(const PermuteArgs& a, hipStream_t st) {
+    if (a.T == 0) return hipSuccess;
+    FQ_KIND_NV_SWITCH(a.a1.q.kind, nv_for(a.H), k_permute_a1, dim3(grid_waves(a.T)), a);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_a2(const SwigluArgs& a, hipStream_t st) {
+    if (a.R == 0) return hipSuccess;
+    FQ_KIND_NV_SWITCH(a.a2.q.kind, nv_for(a.I), k_swiglu_a2, dim3(grid_waves(a.R)), a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+    if (a.T == 0) return hipSuccess;
+    const dim3 grid(grid_waves(a.T));
+    switch (nv_for(a.H)) {
+    case 2: hipLaunchKernelGGL(k_combine<2>, grid, dim3(TPB), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(k_combine<4>, grid, dim3(TPB), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(k_combine<8>, grid, dim3(TPB), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_combine<16>, grid, dim3(TPB), 0, st, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_dy(const PermuteDyArgs& a, hipStream_t st) {
+    if (a.T == 0) return hipSuccess;
+    const dim3 grid(grid_waves(a.T));
+    switch (nv_for(a.H)) {
+    case 2: hipLaunchKernelGGL(k_permute_dy<2>, grid, dim3(TPB), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(k_permute_dy<4>, grid, dim3(TPB), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(k_permute_dy<8>, grid, dim3(TPB), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_permute_dy<16>, grid, dim3(TPB), 0, st, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const SwigluBwdArgs& a, hipStream_t st) {
+    if (a.R == 0) return hipSuccess;
+    const dim3 grid(grid_waves(a.R));
+    switch (a.a2.q.kind) {
+    case K_NONE: hipLaunchKernelGGL(k_swiglu_bwd<K_NONE>, grid, dim3(TPB), 0, st, a); break;
+    case K_NVFP4: hipLaunchKernelGGL(k_swiglu_bwd<K_NVFP4>, grid, dim3(TPB), 0, st, a); break;
+    case K_INT: hipLaunchKernelGGL(k_swiglu_bwd<K_INT>, grid, dim3(TPB), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_swiglu_bwd<K_FP8>, grid, dim3(TPB), 0, st, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_unpermute_a1(const UnpermuteArgs& a, hipStream_t st) {
+    if (a.T == 0) return hipSuccess;
+    FQ_KIND_NV_SWITCH(a.a1.q.kind, nv_for(a.H), k_unpermute_a1, dim3(grid_waves(a.T)), a);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_sum(const float* rowpart, const int32_t* offsets, int E, float* out,
+                              hipStream_t st) {
+    hipLaunchKernelGGL(k_segment_sum, dim3((unsigned)E), dim3(TPB), 0, st, rowpart, offsets, out);
+    return hipGetLastError();
+}
+
+}  // namespace fq

@@ -1,0 +1,201 @@
+"""ctypes binding of libfq.so (include/fq.h): argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI.  torch is used for
+device memory and to hand over the current HIP stream; tensors passed here
+must already live on the GPU with the documented dtype and layout.  There is
+no CPU fallback: if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_int32, c_int64, c_size_t, c_void_p
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfq.so")
+
+# ---- enums (mirror include/fq.h) ------------------------------------------------
+FQ_OK, FQ_E_INVALID, FQ_E_SHAPE, FQ_E_UNSUPPORTED, FQ_E_WORKSPACE, FQ_E_ALIGN, FQ_E_HIP = 0, -1, -2, -3, -4, -5, -6
+FQ_NONE, FQ_NVFP4, FQ_INT, FQ_FP8E4M3 = 0, 1, 2, 3
+FQ_PER_TENSOR, FQ_PER_ROW, FQ_PER_GROUP = 0, 1, 2
+FQ_LEARNABLE, FQ_STATIC, FQ_DYNAMIC = 0, 1, 2
+FORMATS = {"nvfp4": 0, "nvfp4a16": 1, "w4a16": 2, "w8a8": 3, "fp8": 4, "w4afp8": 5}
+BUFFERS = {"counts": 0, "offsets": 1, "row_of": 2, "src_of": 3, "w1hat": 4, "w2hat": 5,
+           "xhat": 6, "z1": 7, "hhat": 8, "yr": 9, "dyr": 100, "dhhat": 101, "dz1": 102,
+           "dxhat": 103, "dw1hat": 104, "dw2hat": 105}
+
+
+class FqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.fq_status_string(status).decode()
+        if status == FQ_E_HIP:
+            msg += ": " + _lib.fq_last_hip_error().decode()
+        super().__init__(f"{where}: {msg} ({status})")
+        self.status = status
+
+
+class QDesc(Structure):
+    _fields_ = [("kind", c_int32), ("gran", c_int32), ("group", c_int32),
+                ("source", c_int32), ("qmin", c_int32), ("qmax", c_int32)]
+
+    def __repr__(self):
+        return (f"QDesc(kind={self.kind}, gran={self.gran}, group={self.group}, "
+                f"source={self.source}, qmin={self.qmin}, qmax={self.qmax})")
+
+
+class LayerDesc(Structure):
+    _fields_ = [("E", c_int64), ("H", c_int64), ("I", c_int64), ("T", c_int64), ("topk", c_int64),
+                ("w1", QDesc), ("w2", QDesc), ("a1", QDesc), ("a2", QDesc)]
+
+
+class ExpertParams(Structure):
+    _fields_ = [("w1", c_void_p), ("w2", c_void_p), ("s_w1", c_void_p), ("t_w1", c_void_p),
+                ("s_w2", c_void_p), ("t_w2", c_void_p), ("s_a1", c_void_p), ("s_a2", c_void_p)]
+
+
+class ExpertGrads(Structure):
+    _fields_ = [("ds_w1", c_void_p), ("ds_w2", c_void_p), ("ds_a1", c_void_p), ("ds_a2", c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m scale_only_quantization_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    Q = POINTER(QDesc)
+    L = POINTER(LayerDesc)
+    sig = {
+        "fq_abi_version": (c_int32, []),
+        "fq_status_string": (c_char_p, [c_int32]),
+        "fq_last_hip_error": (c_char_p, []),
+        "fq_preset": (c_int32, [c_int32, Q, Q, Q, Q]),
+        "fq_tensor_workspace_size": (c_size_t, [Q, c_int64, c_int64, c_int64]),
+        "fq_tensor": (c_int32, [Q, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                c_void_p, c_void_p, c_size_t, c_void_p]),
+        "fq_grouped_expert_saved_size": (c_size_t, [L]),
+        "fq_grouped_expert_workspace_size": (c_size_t, [L]),
+        "fq_grouped_expert_buffer": (c_int32, [L, c_int32, POINTER(c_size_t), POINTER(c_size_t)]),
+        "fq_grouped_expert_fwd": (c_int32, [L, POINTER(ExpertParams), c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
+        "fq_grouped_expert_bwd": (c_int32, [L, POINTER(ExpertParams), c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_size_t, c_void_p, c_void_p,
+                                            POINTER(ExpertGrads), c_void_p, c_size_t, c_void_p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTS = ("fq_abi_version", "fq_status_string", "fq_last_hip_error", "fq_preset",
+           "fq_tensor_workspace_size", "fq_tensor", "fq_grouped_expert_saved_size",
+           "fq_grouped_expert_workspace_size", "fq_grouped_expert_buffer",
+           "fq_grouped_expert_fwd", "fq_grouped_expert_bwd")
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t):
+    """Device address of a tensor (or None), with a dtype sanity check left to callers."""
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != FQ_OK:
+        raise FqError(status, where)
+
+
+def qdesc(kind=FQ_NONE, gran=FQ_PER_TENSOR, group=0, source=FQ_LEARNABLE, qmin=0, qmax=0) -> QDesc:
+    return QDesc(kind, gran, group, source, qmin, qmax)
+
+
+def preset(fmt: str):
+    """(w1, w2, a1, a2) descriptors of a format name."""
+    w1, w2, a1, a2 = QDesc(), QDesc(), QDesc(), QDesc()
+    _check(_lib.fq_preset(FORMATS[fmt], ctypes.byref(w1), ctypes.byref(w2), ctypes.byref(a1),
+                          ctypes.byref(a2)), "fq_preset")
+    return w1, w2, a1, a2
+
+
+# ---- fq_tensor -----------------------------------------------------------------
+def fq_tensor_workspace_size(q: QDesc, batch: int, rows: int, cols: int) -> int:
+    return _lib.fq_tensor_workspace_size(ctypes.byref(q), batch, rows, cols)
+
+
+def fq_tensor(q: QDesc, x, scale=None, tensor_scale=None, y=None, codes=None, block_codes=None,
+              grad_y=None, grad_x=None, grad_scale=None, workspace=None, stream=None, shape=None):
+    """Run fq_tensor on device tensors.  x is bf16 [batch, rows, cols] (or 2D = one batch)."""
+    if shape is None:
+        shape = tuple(x.shape) if x.dim() == 3 else (1,) + tuple(x.shape)
+    batch, rows, cols = shape
+    gfp32 = 0
+    if grad_y is not None:
+        import torch
+        gfp32 = 1 if grad_y.dtype == torch.float32 else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.fq_tensor(ctypes.byref(q), batch, rows, cols, _ptr(x), _ptr(scale), _ptr(tensor_scale),
+                        _ptr(y), _ptr(codes), _ptr(block_codes), _ptr(grad_y), gfp32, _ptr(grad_x),
+                        _ptr(grad_scale), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "fq_tensor")
+
+
+# ---- grouped expert layer ------------------------------------------------------------
+def layer_desc(E, H, I, T, topk, w1: QDesc, w2: QDesc, a1: QDesc, a2: QDesc) -> LayerDesc:
+    return LayerDesc(E, H, I, T, topk, w1, w2, a1, a2)
+
+
+def saved_size(L: LayerDesc) -> int:
+    return _lib.fq_grouped_expert_saved_size(ctypes.byref(L))
+
+
+def workspace_size(L: LayerDesc) -> int:
+    return _lib.fq_grouped_expert_workspace_size(ctypes.byref(L))
+
+
+def buffer(L: LayerDesc, name: str):
+    off, nb = c_size_t(), c_size_t()
+    _check(_lib.fq_grouped_expert_buffer(ctypes.byref(L), BUFFERS[name], ctypes.byref(off),
+                                         ctypes.byref(nb)), "fq_grouped_expert_buffer")
+    return off.value, nb.value
+
+
+def params(w1, w2, s_w1=None, t_w1=None, s_w2=None, t_w2=None, s_a1=None, s_a2=None) -> ExpertParams:
+    return ExpertParams(*[None if t is None else t.data_ptr() for t in
+                          (w1, w2, s_w1, t_w1, s_w2, t_w2, s_a1, s_a2)])
+
+
+def grads(ds_w1=None, ds_w2=None, ds_a1=None, ds_a2=None) -> ExpertGrads:
+    return ExpertGrads(*[None if t is None else t.data_ptr() for t in (ds_w1, ds_w2, ds_a1, ds_a2)])
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def fwd(L: LayerDesc, P: ExpertParams, x, topk_ids, topk_w, y, saved, workspace, stream=None):
+    st = _lib.fq_grouped_expert_fwd(ctypes.byref(L), ctypes.byref(P), _ptr(x), _ptr(topk_ids),
+                                    _ptr(topk_w), _ptr(y), _ptr(saved), _nbytes(saved),
+                                    _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(st, "fq_grouped_expert_fwd")
+
+
+def bwd(L: LayerDesc, P: ExpertParams, x, topk_ids, topk_w, dy, saved, dx, d_topk_w,
+        G: ExpertGrads, workspace, stream=None):
+    st = _lib.fq_grouped_expert_bwd(ctypes.byref(L), ctypes.byref(P), _ptr(x), _ptr(topk_ids),
+                                    _ptr(topk_w), _ptr(dy), _ptr(saved), _nbytes(saved), _ptr(dx),
+                                    _ptr(d_topk_w), ctypes.byref(G), _ptr(workspace),
+                                    _nbytes(workspace), _stream(stream))
+    _check(st, "fq_grouped_expert_bwd")

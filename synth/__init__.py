@@ -163,7 +163,7 @@ def calibrate_act(ids, rows_by_token, E: int, divisor: float, max_rows: int = 25
     """Per-expert activation scale amax / divisor over (up to max_rows of) the
     rows routed to each expert; experts with no rows use the global amax."""
     ids = np.asarray(ids)
-    amax_all = float(np.abs(rows_by_token).max())
+    amax_all = float(np.abs(rows_by_token).max()) if rows_by_token.size else 1.0
     out = np.empty(E, np.float32)
     for e in range(E):
         toks = np.nonzero((ids == e).any(axis=1))[0][:max_rows]
