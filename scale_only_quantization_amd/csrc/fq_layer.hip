@@ -184,7 +184,7 @@ __device__ __forceinline__ float ste8(const float* f, const float* g, float s, f
     for (int i = 0; i < 8; ++i) {
         const Elem el = quant_elem<KIND>(f[i], dv, qmin, qmax);
         part = __builtin_fmaf(g[i], ste_c(el, qmin, qmax), part);
-        gx[i] = (dyn || el.inside) ? g[i] : 0.0f;
+        gx[i] = dyn ? g[i] : g[i] * (el.inside ? 1.0f : 0.0f);   // g * mask (signed zero)
     }
     return part;
 }

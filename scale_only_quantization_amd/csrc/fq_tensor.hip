@@ -170,7 +170,7 @@ __global__ __launch_bounds__(TPB) void k_tensor_bwd(TensorArgs a) {
             for (int i = 0; i < 8; ++i) {
                 Elem e = quant_elem<KIND>(f[i], dv, qmin, qmax);
                 const float c = ste_c(e, qmin, qmax);
-                gx[i] = (DYN || e.inside) ? g[i] : 0.0f;
+                gx[i] = DYN ? g[i] : g[i] * (e.inside ? 1.0f : 0.0f);   // g * mask (signed zero)
                 part = __builtin_fmaf(g[i], c, part);
             }
             if (a.gx) reinterpret_cast<uint4*>(a.gx + grow * a.cols)[v] = pack8(gx);

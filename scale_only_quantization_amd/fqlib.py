@@ -60,6 +60,13 @@ class ExpertGrads(Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m scale_only_quantization_amd.build`")
+    # torch ships its own HIP runtime (same soname, libamdhip64.so.7).  Load it
+    # first so libfq.so binds to that one: two HIP runtimes in one process do
+    # not share devices, memory or streams.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     Q = POINTER(QDesc)
     L = POINTER(LayerDesc)
