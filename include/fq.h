@@ -208,7 +208,21 @@ size_t fq_grouped_expert_workspace_size(const fq_layer_desc* L);
 int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P,
                           const void* x, const int32_t* topk_ids, const float* topk_w,
                           void* y, void* saved, size_t saved_bytes,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* events);
+
+/*
+ * `events` (forward and backward): NULL, or a host array of hipEvent_t handles
+ * (created by the caller) recorded on `stream` at stage boundaries, for timing:
+ * events[i] before stage i and events[n] after the last.  NULL entries are
+ * skipped; a skipped stage still records its boundary.
+ *   forward  (n = FQ_FWD_STAGES): route, W1 fake-quant, W2 fake-quant,
+ *            permute + A1, fc1 GEMM, SwiGLU + A2, fc2 GEMM, combine
+ *   backward (n = FQ_BWD_STAGES): permute dY, fc2 dgrad, fc2 wgrad, SwiGLU + A2
+ *            backward, A2 scale sum, fc1 dgrad, fc1 wgrad, A1 backward +
+ *            unpermute, A1 scale sum, W1 scale grad, W2 scale grad
+ */
+enum { FQ_FWD_STAGES = 8, FQ_BWD_STAGES = 11 };
 
 /*
  * Straight-through backward from dy (device bf16 [T, H]) and the forward's
@@ -224,7 +238,8 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P,
                           const void* x, const int32_t* topk_ids, const float* topk_w,
                           const void* dy, const void* saved, size_t saved_bytes,
                           void* dx, float* d_topk_w, const fq_expert_grads* G,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* events);
 
 /* Location of an intermediate inside `saved` (FQ_BUF_* < 100) or the backward's
  * workspace (>= 100), for inspection between calls: *offset and *bytes.

@@ -189,6 +189,12 @@ int check_aparams(const QParams& q, const float* s) {
     return FQ_OK;
 }
 
+// record the caller's stage-boundary event i (if any) on the stream
+hipError_t mark(void* const* events, int i, hipStream_t st) {
+    if (!events || !events[i]) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+}
+
 template <typename T>
 T* at(void* base, const Section& s) { return reinterpret_cast<T*>(static_cast<char*>(base) + s.off); }
 template <typename T>
@@ -347,7 +353,8 @@ int fq_grouped_expert_buffer(const fq_layer_desc* L, int32_t which, size_t* offs
 
 int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, const void* x,
                           const int32_t* topk_ids, const float* topk_w, void* y, void* saved,
-                          size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+                          size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* events) {
     LayerQ q;
     int s = check_layer(L, &q);
     if (s != FQ_OK) return s;
@@ -382,9 +389,11 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     ra.order = at<int32_t>(saved, lay.order);
     ra.hist = at<int32_t>(workspace, lay.hist);
     ra.local_rank = at<int32_t>(workspace, lay.local_rank);
+    FQ_TRY(mark(events, 0, st));
     FQ_TRY(launch_route(ra, st));
 
     // F3: the whole weight stacks in one pass each
+    FQ_TRY(mark(events, 1, st));
     const uint16_t* w1h = static_cast<const uint16_t*>(P->w1);
     const uint16_t* w2h = static_cast<const uint16_t*>(P->w2);
     if (q.w1.kind != FQ_NONE) {
@@ -400,6 +409,7 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
         FQ_TRY(launch_tensor_fwd(ta, st));
         w1h = ta.y;
     }
+    FQ_TRY(mark(events, 2, st));
     if (q.w2.kind != FQ_NONE) {
         TensorArgs ta{};
         ta.q = q.w2;
@@ -425,6 +435,7 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     pa.H = H;
     pa.E = E;
     pa.a1 = ActQ{q.a1, P->s_a1};
+    FQ_TRY(mark(events, 3, st));
     FQ_TRY(launch_permute_a1(pa, st));
 
     // F4: fc1
@@ -445,6 +456,7 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     g.ldc = 2 * I;
     g.N = 2 * I;
     g.K = H;
+    FQ_TRY(mark(events, 4, st));
     FQ_TRY(launch_gemm_fwd(g, st));
 
     // F5: SwiGLU + A2
@@ -457,6 +469,7 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     sa.I = I;
     sa.E = E;
     sa.a2 = ActQ{q.a2, P->s_a2};
+    FQ_TRY(mark(events, 5, st));
     FQ_TRY(launch_swiglu_a2(sa, st));
 
     // F6: fc2
@@ -469,6 +482,7 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     g.ldc = H;
     g.N = H;
     g.K = I;
+    FQ_TRY(mark(events, 6, st));
     FQ_TRY(launch_gemm_fwd(g, st));
 
     // F7: combine
@@ -480,7 +494,9 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     ca.T = T;
     ca.k = k;
     ca.H = H;
+    FQ_TRY(mark(events, 7, st));
     FQ_TRY(launch_combine(ca, st));
+    FQ_TRY(mark(events, FQ_FWD_STAGES, st));
     return FQ_OK;
 }
 
@@ -488,7 +504,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
                           const int32_t* topk_ids, const float* topk_w, const void* dy,
                           const void* saved, size_t saved_bytes, void* dx, float* d_topk_w,
                           const fq_expert_grads* G, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          void* stream, void* const* events) {
     LayerQ q;
     int s = check_layer(L, &q);
     if (s != FQ_OK) return s;
@@ -538,6 +554,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
     pd.T = T;
     pd.k = k;
     pd.H = H;
+    FQ_TRY(mark(events, 0, st));
     FQ_TRY(launch_permute_dy(pd, st));
 
     GemmArgs g{};
@@ -559,8 +576,10 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
     g.ldc = I;
     g.N = I;
     g.K = H;
+    FQ_TRY(mark(events, 1, st));
     FQ_TRY(launch_gemm_dgrad(g, st));
 
+    FQ_TRY(mark(events, 2, st));
     // B3: fc2 wgrad  dW2^ = dY_r^T H^ (only to form the weight-scale gradient)
     if (G->ds_w2) {
         g.A = dyr;
@@ -587,8 +606,11 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
     sb.I = I;
     sb.E = E;
     sb.a2 = ActQ{q.a2, P->s_a2};
+    FQ_TRY(mark(events, 3, st));
     FQ_TRY(launch_swiglu_bwd(sb, st));
+    FQ_TRY(mark(events, 4, st));
     if (G->ds_a2) FQ_TRY(launch_segment_sum(sb.rowpart, offsets, E, G->ds_a2, st));
+    FQ_TRY(mark(events, 5, st));
 
     const bool need_dxh = dx || G->ds_a1;
     if (need_dxh) {
@@ -604,6 +626,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         g.K = 2 * I;
         FQ_TRY(launch_gemm_dgrad(g, st));
     }
+    FQ_TRY(mark(events, 6, st));
     if (G->ds_w1) {
         // B6: fc1 wgrad  dW1^ = dZ1^T X^
         g.A = dz1;
@@ -617,6 +640,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         g.K = H;
         FQ_TRY(launch_gemm_wgrad(g, st));
     }
+    FQ_TRY(mark(events, 7, st));
     if (need_dxh) {
         // B7: A1 straight-through + unpermute-sum
         UnpermuteArgs ua{};
@@ -632,10 +656,13 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         ua.E = E;
         ua.a1 = ActQ{q.a1, P->s_a1};
         FQ_TRY(launch_unpermute_a1(ua, st));
+        FQ_TRY(mark(events, 8, st));
         if (G->ds_a1) FQ_TRY(launch_segment_sum(ua.rowpart, offsets, E, G->ds_a1, st));
     }
 
+    if (!need_dxh) FQ_TRY(mark(events, 8, st));
     // B8: weight-scale gradients from (W, dW^)
+    FQ_TRY(mark(events, 9, st));
     if (G->ds_w1) {
         TensorArgs ta{};
         ta.q = q.w1;
@@ -651,6 +678,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         ta.rowpart = at<float>(workspace, lay.tws);
         FQ_TRY(launch_tensor_bwd(ta, st));
     }
+    FQ_TRY(mark(events, 10, st));
     if (G->ds_w2) {
         TensorArgs ta{};
         ta.q = q.w2;
@@ -666,6 +694,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         ta.rowpart = at<float>(workspace, lay.tws);
         FQ_TRY(launch_tensor_bwd(ta, st));
     }
+    FQ_TRY(mark(events, FQ_BWD_STAGES, st));
     return FQ_OK;
 }
 

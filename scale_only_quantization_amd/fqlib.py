@@ -83,10 +83,12 @@ def _load():
         "fq_grouped_expert_workspace_size": (c_size_t, [L]),
         "fq_grouped_expert_buffer": (c_int32, [L, c_int32, POINTER(c_size_t), POINTER(c_size_t)]),
         "fq_grouped_expert_fwd": (c_int32, [L, POINTER(ExpertParams), c_void_p, c_void_p, c_void_p,
-                                            c_void_p, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
+                                            c_void_p, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p,
+                                            c_void_p]),
         "fq_grouped_expert_bwd": (c_int32, [L, POINTER(ExpertParams), c_void_p, c_void_p, c_void_p,
                                             c_void_p, c_void_p, c_size_t, c_void_p, c_void_p,
-                                            POINTER(ExpertGrads), c_void_p, c_size_t, c_void_p]),
+                                            POINTER(ExpertGrads), c_void_p, c_size_t, c_void_p,
+                                            c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -192,17 +194,31 @@ def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
 
 
-def fwd(L: LayerDesc, P: ExpertParams, x, topk_ids, topk_w, y, saved, workspace, stream=None):
+FWD_STAGES = ("route", "w1_fq", "w2_fq", "permute_a1", "fc1", "swiglu_a2", "fc2", "combine")
+BWD_STAGES = ("permute_dy", "fc2_dgrad", "fc2_wgrad", "swiglu_bwd", "a2_sum", "fc1_dgrad",
+              "fc1_wgrad", "unpermute_a1", "a1_sum", "w1_scale_grad", "w2_scale_grad")
+
+
+def _events(events):
+    """Host array of hipEvent_t handles (ints) or None."""
+    if events is None:
+        return None
+    return (c_void_p * len(events))(*events)
+
+
+def fwd(L: LayerDesc, P: ExpertParams, x, topk_ids, topk_w, y, saved, workspace, stream=None,
+        events=None):
     st = _lib.fq_grouped_expert_fwd(ctypes.byref(L), ctypes.byref(P), _ptr(x), _ptr(topk_ids),
                                     _ptr(topk_w), _ptr(y), _ptr(saved), _nbytes(saved),
-                                    _ptr(workspace), _nbytes(workspace), _stream(stream))
+                                    _ptr(workspace), _nbytes(workspace), _stream(stream),
+                                    _events(events))
     _check(st, "fq_grouped_expert_fwd")
 
 
 def bwd(L: LayerDesc, P: ExpertParams, x, topk_ids, topk_w, dy, saved, dx, d_topk_w,
-        G: ExpertGrads, workspace, stream=None):
+        G: ExpertGrads, workspace, stream=None, events=None):
     st = _lib.fq_grouped_expert_bwd(ctypes.byref(L), ctypes.byref(P), _ptr(x), _ptr(topk_ids),
                                     _ptr(topk_w), _ptr(dy), _ptr(saved), _nbytes(saved), _ptr(dx),
                                     _ptr(d_topk_w), ctypes.byref(G), _ptr(workspace),
-                                    _nbytes(workspace), _stream(stream))
+                                    _nbytes(workspace), _stream(stream), _events(events))
     _check(st, "fq_grouped_expert_bwd")

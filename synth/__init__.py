@@ -30,10 +30,20 @@ __all__ = ["LayerCase", "CASES", "make_layer", "make_weight_stack", "bf16_round"
 
 
 def bf16_round(x) -> np.ndarray:
-    """Round float32 values to bf16 (nearest, ties to even); float32 out."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    """Round finite float32 values to bf16 (nearest, ties to even); float32 out.
+
+    Works on the bit pattern in uint32 (no overflow for finite inputs), in
+    chunks, on a copy of the input."""
+    out = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = out.reshape(-1).view(np.uint32)
+    step = 1 << 24
+    for i in range(0, u.size, step):
+        c = u[i:i + step]
+        lsb = (c >> 16) & 1
+        c += np.uint32(0x7FFF)
+        c += lsb
+        c &= np.uint32(0xFFFF0000)
+    return out
 
 
 def to_bits(x) -> np.ndarray:

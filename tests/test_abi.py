@@ -143,24 +143,24 @@ def test_layer_validation():
         assert lib.fq_grouped_expert_saved_size(ctypes.byref(L)) == 0
         P = F.ExpertParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
         st = lib.fq_grouped_expert_fwd(ctypes.byref(L), ctypes.byref(P), FAKE, FAKE, FAKE, FAKE,
-                                       FAKE, 1 << 40, FAKE, 1 << 40, None)
+                                       FAKE, 1 << 40, FAKE, 1 << 40, None, None)
         assert st == want, (L.E, L.H, L.I, L.topk, st)
     L = F.layer_desc(8, 256, 128, 64, 2, w1, w2, a1, a2)
     P = F.ExpertParams(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     # missing tensor scale of W1
     Pm = F.ExpertParams(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE)
     assert lib.fq_grouped_expert_fwd(ctypes.byref(L), ctypes.byref(Pm), FAKE, FAKE, FAKE, FAKE, FAKE,
-                                     1 << 40, FAKE, 1 << 40, None) == F.FQ_E_INVALID
+                                     1 << 40, FAKE, 1 << 40, None, None) == F.FQ_E_INVALID
     # buffers too small
     assert lib.fq_grouped_expert_fwd(ctypes.byref(L), ctypes.byref(P), FAKE, FAKE, FAKE, FAKE, FAKE,
-                                     16, FAKE, 1 << 40, None) == F.FQ_E_WORKSPACE
+                                     16, FAKE, 1 << 40, None, None) == F.FQ_E_WORKSPACE
     assert lib.fq_grouped_expert_fwd(ctypes.byref(L), ctypes.byref(P), FAKE, FAKE, FAKE, FAKE, FAKE,
-                                     1 << 40, FAKE, 16, None) == F.FQ_E_WORKSPACE
+                                     1 << 40, FAKE, 16, None, None) == F.FQ_E_WORKSPACE
     # misaligned saved buffer
     assert lib.fq_grouped_expert_fwd(ctypes.byref(L), ctypes.byref(P), FAKE, FAKE, FAKE, FAKE, FAKE + 16,
-                                     1 << 40, FAKE, 1 << 40, None) == F.FQ_E_ALIGN
+                                     1 << 40, FAKE, 1 << 40, None, None) == F.FQ_E_ALIGN
     # a gradient for a quantiser with no parameter (w8a8 activations are dynamic per token)
     Lw = F.layer_desc(8, 256, 128, 64, 2, *F.preset("w8a8"))
     G = F.ExpertGrads(None, None, FAKE, None)
     assert lib.fq_grouped_expert_bwd(ctypes.byref(Lw), ctypes.byref(P), FAKE, FAKE, FAKE, FAKE, FAKE,
-                                     1 << 40, FAKE, None, ctypes.byref(G), FAKE, 1 << 40, None) == F.FQ_E_INVALID
+                                     1 << 40, FAKE, None, ctypes.byref(G), FAKE, 1 << 40, None, None) == F.FQ_E_INVALID
