@@ -88,7 +88,7 @@ struct Section {
 
 struct Layout {
     // saved
-    Section counts, offsets, row_of, src_of, tile_expert, tile_row0, num_tiles, order;
+    Section counts, offsets, row_of, src_of, tile_expert[2], tile_row0[2], num_tiles, order;
     Section w1hat, w2hat, xhat, z1, hhat, yr;
     size_t saved = 0;
     // workspace
@@ -138,15 +138,17 @@ int check_layer(const fq_layer_desc* L, LayerQ* q) {
 Layout layout(const fq_layer_desc* L, const LayerQ& q) {
     Layout y;
     const int64_t E = L->E, H = L->H, I = L->I, R = L->T * L->topk;
-    const int64_t mt = max_mtiles(R, (int)E);
     size_t c = 0;
     place(y.counts, E * 4, c);
     place(y.offsets, (E + 1) * 4, c);
     place(y.row_of, R * 4, c);
     place(y.src_of, R * 4, c);
-    place(y.tile_expert, mt * 4, c);
-    place(y.tile_row0, mt * 4, c);
-    place(y.num_tiles, 4, c);
+    for (int h = 0; h < 2; ++h) {
+        const int64_t mt = max_mtiles(R, (int)E, TILE_HEIGHTS[h]);
+        place(y.tile_expert[h], mt * 4, c);
+        place(y.tile_row0[h], mt * 4, c);
+    }
+    place(y.num_tiles, 2 * 4, c);
     place(y.order, E * 4, c);
     place(y.w1hat, q.w1.kind != FQ_NONE ? (size_t)E * 2 * I * H * 2 : 0, c);
     place(y.w2hat, q.w2.kind != FQ_NONE ? (size_t)E * H * I * 2 : 0, c);
@@ -383,9 +385,11 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     ra.offsets = at<int32_t>(saved, lay.offsets);
     ra.row_of = at<int32_t>(saved, lay.row_of);
     ra.src_of = at<int32_t>(saved, lay.src_of);
-    ra.tile_expert = at<int32_t>(saved, lay.tile_expert);
-    ra.tile_row0 = at<int32_t>(saved, lay.tile_row0);
-    ra.num_tiles = at<int32_t>(saved, lay.num_tiles);
+    for (int h = 0; h < 2; ++h) {
+        ra.tables[h].tile_expert = at<int32_t>(saved, lay.tile_expert[h]);
+        ra.tables[h].tile_row0 = at<int32_t>(saved, lay.tile_row0[h]);
+        ra.tables[h].num_tiles = at<int32_t>(saved, lay.num_tiles) + h;
+    }
     ra.order = at<int32_t>(saved, lay.order);
     ra.hist = at<int32_t>(workspace, lay.hist);
     ra.local_rank = at<int32_t>(workspace, lay.local_rank);
@@ -443,9 +447,8 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     g.R = R;
     g.E = E;
     g.offsets = ra.offsets;
-    g.tile_expert = ra.tile_expert;
-    g.tile_row0 = ra.tile_row0;
-    g.num_tiles = ra.num_tiles;
+    g.tables[0] = ra.tables[0];
+    g.tables[1] = ra.tables[1];
     g.order = ra.order;
     g.A = pa.xhat;
     g.lda = H;
@@ -561,9 +564,11 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
     g.R = R;
     g.E = E;
     g.offsets = offsets;
-    g.tile_expert = at<int32_t>(saved, lay.tile_expert);
-    g.tile_row0 = at<int32_t>(saved, lay.tile_row0);
-    g.num_tiles = at<int32_t>(saved, lay.num_tiles);
+    for (int h = 0; h < 2; ++h) {
+        g.tables[h].tile_expert = const_cast<int32_t*>(at<int32_t>(saved, lay.tile_expert[h]));
+        g.tables[h].tile_row0 = const_cast<int32_t*>(at<int32_t>(saved, lay.tile_row0[h]));
+        g.tables[h].num_tiles = const_cast<int32_t*>(at<int32_t>(saved, lay.num_tiles)) + h;
+    }
     g.order = at<int32_t>(saved, lay.order);
 
     // B2: fc2 dgrad  dH^ = dY_r W2^

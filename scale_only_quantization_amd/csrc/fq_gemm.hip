@@ -5,214 +5,316 @@
 //   FWD    C[r, n]    = sum_k A[r, k] B_e[n, k]      A routed rows, B [N, K]   (bf16 out)
 //   DGRAD  C[r, n]    = sum_k A[r, k] B_e[k, n]      B stored [K, N]           (bf16 out)
 //   WGRAD  C_e[i, j]  = sum_r A[r, i] B[r, j]        rows r of expert e        (fp32 out)
-// Tiles: 128 x 128 outputs x 64 reduction per step, 256 threads = 4 waves as
-// 2 x 2, each wave 64 x 64 outputs = 2 x 2 v_mfma_f32_32x32x16_bf16.  Both
-// operand tiles live in LDS as [128 rows][64 reduction] bf16 (128 B per row),
-// the 16-byte chunk index XOR-swizzled with (row ^ row >> 3) & 7 so the MFMA
-// fragment reads (32 rows, one chunk) and the transposing writes of
-// MN-contiguous operands both spread over the banks.  Two LDS stages: the next
-// tile's global loads are in flight while the current one is multiplied.
-// FWD/DGRAD row tiles come from the device-side tile table (expert, first row)
+//
+// Block: 256 threads = 4 waves as 2 x 2; each wave owns WTM x WTN 32 x 32
+// output tiles (v_mfma_f32_32x32x16_bf16), so the block tile is
+// (64 WTM) x (64 WTN); with 4 x 4 a wave holds 128 x 128 fp32 accumulators
+// (256 per lane), which keeps LDS reads per MFMA low.
+//
+// Operands go from global memory straight into LDS (buffer_load ... lds,
+// 16 B per lane; one wave instruction fills 1 KB), through buffer resources
+// bounded to the valid rows, so rows past the routed rows or past an expert's
+// rows (the WGRAD reduction tail) read as zero.  A reduction step is 32 deep;
+// S LDS stages are in flight, so a tile's loads are issued S-1 steps before
+// its MFMAs.
+//   K-contiguous operand: LDS [rows][32] (64 B per row), the 16-B chunk index
+//     XOR (row >> 1) & 3; a fragment (8 consecutive k of one row) is one
+//     ds_read_b128, and 8 consecutive rows at one chunk cover all banks.
+//   Row-contiguous operand: LDS [32][rows] as in memory, the 16-B chunk index
+//     XOR 2 (k & 3); a fragment is two ds_read_b64_tr_b16: inside each group
+//     of 16 lanes, lane i points at k-row kb + i/4, columns mb + 4(i%4) .. +3,
+//     and lane j receives k = kb .. kb+3 of column mb + j.
+// FWD/DGRAD row tiles come from a device-side tile table (expert, first row)
 // built by the routing scan, so no host read-back of the counts is needed;
-// WGRAD visits experts in descending row count (longest reductions first).
+// WGRAD visits experts in descending row count.
 #include <type_traits>
 
 #include "fq_common.h"
 #include "fq_internal.h"
+
+#ifndef GEMM_BK_BIG
+#define GEMM_BK_BIG 64
+#define GEMM_S_BIG 2
+#endif
+#ifndef GEMM_XCD
+#define GEMM_XCD 1          // contiguous tile runs per XCD for FWD/DGRAD
+#endif
+#ifndef GEMM_WVM
+#define GEMM_WVM 2          // waves of the large tile along rows x columns
+#define GEMM_WVN 2
+#endif
+#ifndef GEMM_SCHED
+#define GEMM_SCHED 1        // interleave fragment reads with MFMAs explicitly
+#endif
 
 namespace fq {
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_t;
 
-constexpr int BM = GEMM_BM;      // 128
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int NT = 256;
-constexpr int TILE_BYTES = 128 * BK * 2;   // one operand tile, 16 KB
 
 enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2 };
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int ch) { return row * 128 + ((ch ^ swz(row)) << 4); }
+// Buffer resource over [base, base + bytes): loads outside read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0xFFFFFFF0ll) bytes = 0xFFFFFFF0ll;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes,
+                                             0x00020000);
+}
 
-// Operand whose reduction index is contiguous in memory: element (row, k) at
-// base_row[row] + k.  Thread t moves rows t/8 + 32p (p < 4), 16-B chunk t%8.
-struct KLoader {
-    const uint16_t* rowp[4];
-    uint4 reg[4];
-    __device__ __forceinline__ void load(int k0) {
-        const int ch = threadIdx.x & 7;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) reg[p] = *reinterpret_cast<const uint4*>(rowp[p] + k0 + ch * 8);
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// K-contiguous operand tile [ROWS][BK]: element (row, k) at byte row*ld2 + 2k
+// of the resource.  Rows of 2 BK bytes; each 1-KB wave load covers 512/BK rows.
+// Swizzle: chunk ^ (row >> 1) & 3 for 64-B rows, chunk ^ (row ^ row >> 3) & 7
+// for 128-B rows, so 8 consecutive rows at one chunk cover all banks.
+template <int ROWS, int BK, int NW>
+struct KTile {
+    static constexpr int BYTES = ROWS * BK * 2;
+    static constexpr int PER_WAVE = BYTES / 1024 / NW;
+    static constexpr int CPR = BK / 8;                 // 16-B chunks per row
+    __device__ static __forceinline__ int swz(int row) {
+        return BK == 32 ? ((row >> 1) & 3) : ((row ^ (row >> 3)) & 7);
     }
-    __device__ __forceinline__ void store(char* lds) const {
-        const int ch = threadIdx.x & 7;
+    __device__ static __forceinline__ int off(int row, int ch) {   // byte offset of 16-B chunk
+        return row * (2 * BK) + ((ch ^ swz(row)) << 4);
+    }
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t voff[PER_WAVE];
+    __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t r, int64_t ld) {
+        rs = r;
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int row = (threadIdx.x >> 3) + 32 * p;
-            *reinterpret_cast<uint4*>(lds + lds_off(row, ch)) = reg[p];
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int blk = NW * i + w;                   // 1-KB block
+            const int row = blk * (64 / CPR) + lane / CPR;
+            const int lc = (lane % CPR) ^ swz(row);       // logical chunk stored at this position
+            voff[i] = (uint32_t)(row * ld * 2 + lc * 16);
         }
+    }
+    __device__ __forceinline__ void issue(lds_t* tile, int k0) {
+        const int w = wave_id();
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + w) * 1024, 16, voff[i], k0 * 2, 0, 0);
+    }
+    // fragment of the 32x32x16 MFMA: row `row0 + lane%32`, k = 16 kk + 8 (lane/32) .. +7
+    __device__ static __forceinline__ bf16x8 frag(const lds_t* tile, int row0, int kk) {
+        const int lane = threadIdx.x & 63;
+        const int row = row0 + (lane & 31);
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            tile + off(row, kk * 2 + (lane >> 5)));
     }
 };
 
-// Operand whose row index is contiguous: element (row, k) at base[k*ld + row].
-// Thread t reads 4 consecutive k rows (kg = t/16) of 8 consecutive rows
-// (chunk t%16) and writes them transposed: 8 rows x 4 k = 8 ds_write_b64.
-// k >= kmax reads as zero (end of an expert's rows).
-struct MNLoader {
-    const uint16_t* base;
-    int64_t ld;
-    int kmax;
-    uint4 reg[4];
-    __device__ __forceinline__ void load(int k0) {
-        const int nc = threadIdx.x & 15, kg = threadIdx.x >> 4;
+// Row-contiguous operand tile [BK][ROWS] (stored as in memory): element
+// (row, k) at byte k*ld2 + 2*row of the resource.  Each 1-KB wave load covers
+// 1024 / (2 ROWS) k-rows.
+template <int ROWS, int BK, int NW>
+struct MNTile {
+    static constexpr int BYTES = ROWS * BK * 2;
+    static constexpr int PER_WAVE = BYTES / 1024 / NW;
+    static constexpr int RB = ROWS * 2;               // bytes per k-row
+    __device__ static __forceinline__ int off(int k, int byte) {   // swizzled byte offset
+        return k * RB + (((byte >> 4) ^ ((k & 3) << 1)) << 4) + (byte & 15);
+    }
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t voff[PER_WAVE];
+    uint32_t ld2;
+    __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t r, int64_t ld) {
+        rs = r;
+        ld2 = (uint32_t)(ld * 2);
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = k0 + kg * 4 + i;
-            reg[i] = k < kmax ? *reinterpret_cast<const uint4*>(base + (int64_t)k * ld + nc * 8)
-                              : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int pos = (NW * i + w) * 1024 + lane * 16;  // byte position in the tile
+            const int k = pos / RB;
+            const int pc = (pos % RB) >> 4;
+            const int lc = pc ^ ((k & 3) << 1);
+            voff[i] = (uint32_t)(k * ld * 2 + lc * 16);
         }
     }
-    __device__ __forceinline__ void store(char* lds) const {
-        const int nc = threadIdx.x & 15, kg = threadIdx.x >> 4;
-        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&reg[0]);
-        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&reg[1]);
-        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&reg[2]);
-        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&reg[3]);
+    __device__ __forceinline__ void issue(lds_t* tile, int k0) {
+        const int w = wave_id();
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = nc * 8 + j;
-            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-            uint2 v;
-            v.x = __builtin_amdgcn_perm(r1[j >> 1], r0[j >> 1], sel);
-            v.y = __builtin_amdgcn_perm(r3[j >> 1], r2[j >> 1], sel);
-            *reinterpret_cast<uint2*>(lds + lds_off(row, kg >> 1) + (kg & 1) * 8) = v;
-        }
+        for (int i = 0; i < PER_WAVE; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + w) * 1024, 16,
+                                                     voff[i] + (uint32_t)k0 * ld2, 0, 0, 0);
+    }
+    __device__ static __forceinline__ bf16x8 frag(const lds_t* tile, int row0, int kk) {
+        const int lane = threadIdx.x & 63;
+        const int i = lane & 15;
+        const int mb = row0 + ((lane >> 4) & 1) * 16;
+        const int kb = kk * 16 + (lane >> 5) * 8 + (i >> 2);
+        const int byte = (mb + 4 * (i & 3)) * 2;
+        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+        typedef __attribute__((address_space(3))) v4bf lds4;
+        lds_t* t = const_cast<lds_t*>(tile);
+        const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(t + off(kb, byte))));
+        const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(t + off(kb + 4, byte))));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 };
 
-template <int MODE>
-__global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) char smem[2][2][TILE_BYTES];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+// Block -> tile with XCD locality: workgroups are dealt to the 8 XCDs (each
+// with its own L2) round-robin, so XCD x = id % 8 is given the contiguous run
+// of tiles [x * chunk, (x + 1) * chunk), chunk = ceil(tiles / 8); tiles that
+// share operands (the N tiles of one row tile, the row tiles of one expert)
+// then meet in the same L2.  Returns -1 for ids past the tile count.
+__device__ __forceinline__ int xcd_tile(int id, int grid, int tiles) {
+    const int chunk = (tiles + 7) / 8;
+    const int t = (id % 8) * chunk + id / 8;
+    return (id / 8 < chunk && t < tiles) ? t : -1;
+}
+
+template <int MODE, int WVM, int WVN, int WTM, int WTN, int BK, int S>
+__global__ __launch_bounds__(64 * WVM * WVN) void k_gemm(GemmArgs g) {
+    constexpr int NW = WVM * WVN;
+    constexpr int BM = 32 * WTM * WVM, BN = 32 * WTN * WVN;
+    typedef typename std::conditional<MODE == WGRAD, MNTile<BM, BK, NW>, KTile<BM, BK, NW>>::type ATile;
+    typedef typename std::conditional<MODE == FWD, KTile<BN, BK, NW>, MNTile<BN, BK, NW>>::type BTile;
+    constexpr int A_BYTES = ATile::BYTES, STAGE = ATile::BYTES + BTile::BYTES;
+    constexpr int LOADS = ATile::PER_WAVE + BTile::PER_WAVE;     // wave load instructions per stage
+    static_assert(S >= 2 && S <= 4, "stages");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE];
+    lds_t* smem = (lds_t*)smem_raw;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WVN, wn = wave % WVN;
 
     int e, nk;
     int64_t m0 = 0, m_end = 0;      // FWD/DGRAD: routed row range of the tile's expert
     int n0, i0 = 0;
-    typedef typename std::conditional<MODE == WGRAD, MNLoader, KLoader>::type ALoad;
-    typedef typename std::conditional<MODE == FWD, KLoader, MNLoader>::type BLoad;
-    ALoad la;
-    BLoad lb;
+    ATile la;
+    BTile lb;
 
     if (MODE != WGRAD) {
         const int ntn = g.N / BN;
-        const int mt = blockIdx.x / ntn;
-        const int nt = blockIdx.x - mt * ntn;
-        if (mt >= g.num_tiles[0]) return;
+        const int tile = GEMM_XCD ? xcd_tile(blockIdx.x, gridDim.x, g.num_tiles[0] * ntn) : (int)blockIdx.x;
+        if (tile < 0 || tile >= g.num_tiles[0] * ntn) return;
+        const int mt = tile / ntn;
+        const int nt = tile - mt * ntn;
         e = min(max(g.tile_expert[mt], 0), g.E - 1);
         m0 = g.tile_row0[mt];
         m_end = min((int64_t)g.offsets[e + 1], g.R);
         n0 = nt * BN;
         nk = g.K / BK;
-        const int ch_row = tid >> 3;
-        if constexpr (MODE != WGRAD) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                int64_t r = m0 + ch_row + 32 * p;
-                if (r > g.R - 1) r = g.R - 1;
-                la.rowp[p] = g.A + r * g.lda;
-            }
-        }
+        // rows past the routed rows read as zero (their outputs are not stored)
+        la.init(make_rsrc(g.A + m0 * g.lda, (g.R - m0) * g.lda * 2), g.lda);
         const uint16_t* Be = g.B + (int64_t)e * g.strideB;
-        if constexpr (MODE == FWD) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) lb.rowp[p] = Be + (int64_t)(n0 + ch_row + 32 * p) * g.ldb;
-        } else if constexpr (MODE == DGRAD) {
-            lb.base = Be + n0;
-            lb.ld = g.ldb;
-            lb.kmax = g.K;
-        }
+        if constexpr (MODE == FWD)
+            lb.init(make_rsrc(Be + (int64_t)n0 * g.ldb, (int64_t)BN * g.ldb * 2), g.ldb);
+        else
+            lb.init(make_rsrc(Be + n0, ((int64_t)g.K - 1) * g.ldb * 2 + (int64_t)BN * 2), g.ldb);
     } else {
         const int tj = g.K / BN;              // output [N, K] per expert
         const int tpe = (g.N / BM) * tj;
-        const int eo = blockIdx.x / tpe;
-        const int tt = blockIdx.x - eo * tpe;
+        // longest reductions first, dealt round-robin over the XCDs
+        const int tile = blockIdx.x;
+        if (tile >= g.E * tpe) return;
+        const int eo = tile / tpe;
+        const int tt = tile - eo * tpe;
         e = min(max(g.order[eo], 0), g.E - 1);
         i0 = (tt / tj) * BM;
         n0 = (tt - (tt / tj) * tj) * BN;
         const int64_t rb = g.offsets[e];
         const int me = (int)(min((int64_t)g.offsets[e + 1], g.R) - rb);
         nk = (me + BK - 1) / BK;
-        if constexpr (MODE == WGRAD) {
-            la.base = g.A + rb * g.lda + i0;
-            la.ld = g.lda;
-            la.kmax = me;
-            lb.base = g.B + rb * g.ldb + n0;
-            lb.ld = g.ldb;
-            lb.kmax = me;
-        }
+        // bounded to the expert's rows: the last reduction step's tail reads zeros
+        la.init(make_rsrc(g.A + rb * g.lda + i0, (int64_t)me * g.lda * 2 - i0 * 2), g.lda);
+        lb.init(make_rsrc(g.B + rb * g.ldb + n0, (int64_t)me * g.ldb * 2 - n0 * 2), g.ldb);
     }
 
-    f32x16 acc[2][2];
+    f32x16 acc[WTM][WTN];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < WTM; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < WTN; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-    if (nk > 0) {
-        la.load(0);
-        lb.load(0);
-        la.store(smem[0][0]);
-        lb.store(smem[0][1]);
-        __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            la.load((kt + 1) * BK);
-            lb.load((kt + 1) * BK);
-        }
-        const char* sa = smem[cur][0];
-        const char* sb = smem[cur][1];
+    // MFMAs of one 32-deep step: fragments of the second 16-deep half are
+    // read while the first half's MFMAs run.
+    auto compute = [&](const lds_t* st) {
+        const lds_t* sa = st;
+        const lds_t* sb = st + A_BYTES;
+        bf16x8 af[2][WTM], bfr[2][WTN];
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int ch = kk * 2 + (lane >> 5);
-            bf16x8 af[2], bfr[2];
+        for (int kk = 0; kk <= BK / 16; ++kk) {
+            if (kk < BK / 16) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                af[t] = *reinterpret_cast<const bf16x8*>(sa + lds_off(wm * 64 + t * 32 + (lane & 31), ch));
-                bfr[t] = *reinterpret_cast<const bf16x8*>(sb + lds_off(wn * 64 + t * 32 + (lane & 31), ch));
+                for (int t = 0; t < WTM; ++t) af[kk & 1][t] = ATile::frag(sa, wm * 32 * WTM + t * 32, kk);
+#pragma unroll
+                for (int t = 0; t < WTN; ++t) bfr[kk & 1][t] = BTile::frag(sb, wn * 32 * WTN + t * 32, kk);
             }
+            if (kk > 0) {
+                const int s = (kk - 1) & 1;
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti)
+                for (int ti = 0; ti < WTM; ++ti)
 #pragma unroll
-                for (int tj = 0; tj < 2; ++tj)
-                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[tj], af[ti], acc[ti][tj], 0, 0, 0);
+                    for (int tj = 0; tj < WTN; ++tj)
+                        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s][tj], af[s][ti], acc[ti][tj],
+                                                                              0, 0, 0);
+            }
         }
-        if (kt + 1 < nk) {
-            la.store(smem[cur ^ 1][0]);
-            lb.store(smem[cur ^ 1][1]);
+        if (GEMM_SCHED) {
+            // sub-step 0 reads, then each sub-step's MFMAs interleaved with the
+            // next sub-step's reads (a row-contiguous fragment is two reads)
+            constexpr int NR = WTM * (std::is_same<ATile, KTile<BM, BK, NW>>::value ? 1 : 2) +
+                               WTN * (std::is_same<BTile, KTile<BN, BK, NW>>::value ? 1 : 2);
+            constexpr int NM = WTM * WTN;
+            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+            for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, NM / NR > 0 ? NM / NR : 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+        }
+    };
+    auto stage = [&](int s) { return smem + (s % S) * STAGE; };
+    auto issue = [&](int kt) {
+        la.issue(stage(kt), kt * BK);
+        lb.issue(stage(kt) + A_BYTES, kt * BK);
+    };
+
+    // prologue: S-1 steps in flight
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+        if (p < nk) issue(p);
+    for (int kt = 0; kt < nk; ++kt) {
+        // this wave's loads of step kt are done once at most the loads of the
+        // S-2 later steps are outstanding; the barrier then covers every wave
+        if (kt + S - 2 < nk) {
+            if constexpr (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else if constexpr (S == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         __syncthreads();
+        // the stage step kt+S-1 overwrites was read in step kt-1, finished by every wave
+        if (kt + S - 1 < nk) issue(kt + S - 1);
+        compute(stage(kt));
     }
 
     // epilogue: lane holds C[m = lane%32][n = 8*(v/4) + 4*(lane/32) + v%4] of each 32x32 tile
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-        const int ml = wm * 64 + ti * 32 + (lane & 31);
+    for (int ti = 0; ti < WTM; ++ti) {
+        const int ml = wm * 32 * WTM + ti * 32 + (lane & 31);
 #pragma unroll
-        for (int tj = 0; tj < 2; ++tj) {
+        for (int tj = 0; tj < WTN; ++tj) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int nl = wn * 64 + tj * 32 + 8 * q + 4 * (lane >> 5);
+                const int nl = wn * 32 * WTN + tj * 32 + 8 * q + 4 * (lane >> 5);
                 const float c0 = acc[ti][tj][4 * q], c1 = acc[ti][tj][4 * q + 1];
                 const float c2 = acc[ti][tj][4 * q + 2], c3 = acc[ti][tj][4 * q + 3];
                 if (MODE == WGRAD) {
@@ -231,26 +333,52 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
     }
 }
 
+// Large tile: 256 x 256 outputs, as WVM_BIG x WVN_BIG waves of
+// (256 / WVM_BIG) x (256 / WVN_BIG); small tile: 128 x 128, 2 x 2 waves.
+constexpr int BK_BIG = GEMM_BK_BIG, S_BIG = GEMM_S_BIG, BK_SMALL = 32, S_SMALL = 3;
+constexpr int WVM_BIG = GEMM_WVM, WVN_BIG = GEMM_WVN;
+constexpr int WTM_BIG = 8 / WVM_BIG, WTN_BIG = 8 / WVN_BIG;
+#define FQ_BIG(MODE) k_gemm<MODE, WVM_BIG, WVN_BIG, WTM_BIG, WTN_BIG, BK_BIG, S_BIG>
+#define FQ_SMALL(MODE) k_gemm<MODE, 2, 2, 2, 2, BK_SMALL, S_SMALL>
+
+// Explicit instantiations: without them the host pass does not emit every
+// launch stub for this template.
+template __global__ void FQ_BIG(FWD)(GemmArgs);
+template __global__ void FQ_SMALL(FWD)(GemmArgs);
+template __global__ void FQ_BIG(DGRAD)(GemmArgs);
+template __global__ void FQ_SMALL(DGRAD)(GemmArgs);
+template __global__ void FQ_BIG(WGRAD)(GemmArgs);
+template __global__ void FQ_SMALL(WGRAD)(GemmArgs);
+
+// Large tiles where the shapes allow, 128 x 128 otherwise.
+template <int MODE>
+hipError_t launch(const GemmArgs& g, hipStream_t st) {
+    const bool big_m = MODE == WGRAD ? (g.N % 256 == 0) : true;
+    const bool big_n = (MODE == WGRAD ? g.K : g.N) % 256 == 0;
+    const int big = (big_m && big_n) ? 1 : 0;
+    GemmArgs a = g;
+    int64_t blocks;
+    if (MODE != WGRAD) {
+        if (g.R == 0) return hipSuccess;
+        a.tile_expert = g.tables[big].tile_expert;
+        a.tile_row0 = g.tables[big].tile_row0;
+        a.num_tiles = g.tables[big].num_tiles;
+        const int bm = big ? 256 : 128;
+        blocks = max_mtiles(g.R, g.E, bm) * (g.N / bm);
+    } else {
+        const int t = big ? 256 : 128;
+        blocks = (int64_t)g.E * (g.N / t) * (g.K / t);
+    }
+    blocks = (blocks + 7) / 8 * 8;       // a whole number of blocks per XCD
+    if (big) hipLaunchKernelGGL((FQ_BIG(MODE)), dim3((unsigned)blocks), dim3(64 * WVM_BIG * WVN_BIG), 0, st, a);
+    else hipLaunchKernelGGL((FQ_SMALL(MODE)), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_gemm_fwd(const GemmArgs& g, hipStream_t st) {
-    if (g.R == 0) return hipSuccess;
-    const int64_t blocks = max_mtiles(g.R, g.E) * (g.N / BN);
-    hipLaunchKernelGGL(k_gemm<FWD>, dim3((unsigned)blocks), dim3(NT), 0, st, g);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemm_dgrad(const GemmArgs& g, hipStream_t st) {
-    if (g.R == 0) return hipSuccess;
-    const int64_t blocks = max_mtiles(g.R, g.E) * (g.N / BN);
-    hipLaunchKernelGGL(k_gemm<DGRAD>, dim3((unsigned)blocks), dim3(NT), 0, st, g);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemm_wgrad(const GemmArgs& g, hipStream_t st) {
-    const int64_t blocks = (int64_t)g.E * (g.N / BM) * (g.K / BN);
-    hipLaunchKernelGGL(k_gemm<WGRAD>, dim3((unsigned)blocks), dim3(NT), 0, st, g);
-    return hipGetLastError();
-}
+hipError_t launch_gemm_fwd(const GemmArgs& g, hipStream_t st) { return launch<FWD>(g, st); }
+hipError_t launch_gemm_dgrad(const GemmArgs& g, hipStream_t st) { return launch<DGRAD>(g, st); }
+hipError_t launch_gemm_wgrad(const GemmArgs& g, hipStream_t st) { return launch<WGRAD>(g, st); }
 
 }  // namespace fq

@@ -35,7 +35,14 @@ hipError_t launch_tensor_bwd(const TensorArgs& a, hipStream_t st);
 size_t tensor_workspace_bytes(const QParams& q, int64_t batch, int64_t rows);
 
 // ------------------------------------------------------------------ layer ---
-constexpr int GEMM_BM = 128;          // routed rows per GEMM tile (tile table granularity)
+// Row-tile tables of the routed rows, one per GEMM tile height (128, 256):
+// tile i covers rows [row0[i], row0[i] + height) of expert[i], clipped to it.
+struct TileTable {
+    int32_t* tile_expert;  // [max_mtiles(R, E, height)]
+    int32_t* tile_row0;
+    int32_t* num_tiles;    // [1]
+};
+constexpr int TILE_HEIGHTS[2] = {128, 256};
 
 struct RouteArgs {
     const int32_t* ids;    // [R]
@@ -45,16 +52,14 @@ struct RouteArgs {
     int32_t* offsets;      // [E+1]
     int32_t* row_of;       // [R]
     int32_t* src_of;       // [R]
-    int32_t* tile_expert;  // [max_tiles]
-    int32_t* tile_row0;    // [max_tiles]
-    int32_t* num_tiles;    // [1]
+    TileTable tables[2];   // heights 128 and 256
     int32_t* order;        // [E] experts by descending count
     int32_t* hist;         // workspace [nblk, E]
     int32_t* local_rank;   // workspace [R]
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 int64_t route_blocks(int64_t R);
-int64_t max_mtiles(int64_t R, int E);
+int64_t max_mtiles(int64_t R, int E, int height);
 
 // Activation quantiser of the layer (per expert parameter vector or none).
 struct ActQ {
@@ -148,7 +153,8 @@ struct GemmArgs {
     int64_t R;
     int E;
     const int32_t* offsets;
-    const int32_t* tile_expert;
+    TileTable tables[2];          // row tiles of height 128 and 256
+    const int32_t* tile_expert;   // the table the launched kernel uses
     const int32_t* tile_row0;
     const int32_t* num_tiles;
     const int32_t* order;

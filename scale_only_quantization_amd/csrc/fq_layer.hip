@@ -76,15 +76,16 @@ __global__ __launch_bounds__(TPB) void k_route_local(const int32_t* ids, int64_t
     }
 }
 
-// One block: per-expert counts, block bases, offsets, the GEMM row-tile table
-// and the experts ordered by descending count (ties by id).
+// One block: per-expert counts, block bases, offsets, the GEMM row-tile
+// tables (heights 128 and 256) and the experts ordered by descending count
+// (ties by id).
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, int E, int32_t* counts,
-                                                     int32_t* offsets, int32_t* tile_expert,
-                                                     int32_t* tile_row0, int32_t* num_tiles,
+                                                     int32_t* offsets, TileTable t128, TileTable t256,
                                                      int32_t* order) {
     __shared__ int32_t s_cnt[1024];
     __shared__ int32_t s_a[1024];
     __shared__ int32_t s_b[1024];
+    __shared__ int32_t s_c[1024];
     const int e = threadIdx.x;
     int running = 0;
     if (e < E) {
@@ -95,32 +96,40 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
         }
     }
     const int cnt = e < E ? running : 0;
-    const int mt = (cnt + GEMM_BM - 1) / GEMM_BM;
+    const int m1 = (cnt + 127) / 128, m2 = (cnt + 255) / 256;
     s_cnt[e] = cnt;
     s_a[e] = cnt;
-    s_b[e] = mt;
+    s_b[e] = m1;
+    s_c[e] = m2;
     __syncthreads();
-    // inclusive Hillis-Steele scans of counts and of row tiles
+    // inclusive Hillis-Steele scans of counts and of both row-tile counts
     for (int d = 1; d < 1024; d <<= 1) {
         const int va = e >= d ? s_a[e - d] : 0;
         const int vb = e >= d ? s_b[e - d] : 0;
+        const int vc = e >= d ? s_c[e - d] : 0;
         __syncthreads();
         s_a[e] += va;
         s_b[e] += vb;
+        s_c[e] += vc;
         __syncthreads();
     }
     const int off = s_a[e] - cnt;
-    const int tstart = s_b[e] - mt;
+    const int ts1 = s_b[e] - m1, ts2 = s_c[e] - m2;
     if (e < E) {
         counts[e] = cnt;
         offsets[e] = off;
         if (e == E - 1) {
             offsets[E] = off + cnt;
-            num_tiles[0] = tstart + mt;
+            t128.num_tiles[0] = ts1 + m1;
+            t256.num_tiles[0] = ts2 + m2;
         }
-        for (int i = 0; i < mt; ++i) {
-            tile_expert[tstart + i] = e;
-            tile_row0[tstart + i] = off + i * GEMM_BM;
+        for (int i = 0; i < m1; ++i) {
+            t128.tile_expert[ts1 + i] = e;
+            t128.tile_row0[ts1 + i] = off + i * 128;
+        }
+        for (int i = 0; i < m2; ++i) {
+            t256.tile_expert[ts2 + i] = e;
+            t256.tile_row0[ts2 + i] = off + i * 256;
         }
         int rank = 0;
         for (int o = 0; o < E; ++o) {
@@ -581,7 +590,7 @@ int nv_for(int H) { return H <= 1024 ? 2 : H <= 2048 ? 4 : H <= 4096 ? 8 : 16; }
 }  // namespace
 
 int64_t route_blocks(int64_t R) { return (R + RB - 1) / RB; }
-int64_t max_mtiles(int64_t R, int E) { return (R + GEMM_BM - 1) / GEMM_BM + E; }
+int64_t max_mtiles(int64_t R, int E, int height) { return (R + height - 1) / height + E; }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     if (a.E > 1024) return hipErrorInvalidValue;
@@ -595,7 +604,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
         if (err != hipSuccess) return err;
     }
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, a.hist, (int)nblk, a.E, a.counts,
-                       a.offsets, a.tile_expert, a.tile_row0, a.num_tiles, a.order);
+                       a.offsets, a.tables[0], a.tables[1], a.order);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nblk == 0) return err;
     hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nblk), dim3(TPB), 0, st, a.ids, a.R, a.E, a.hist,

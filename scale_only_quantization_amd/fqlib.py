@@ -12,7 +12,8 @@ import os
 from ctypes import POINTER, Structure, c_char_p, c_int32, c_int64, c_size_t, c_void_p
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfq.so")
+# FQ_LIB selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("FQ_LIB") or os.path.join(_PKG, "libfq.so")
 
 # ---- enums (mirror include/fq.h) ------------------------------------------------
 FQ_OK, FQ_E_INVALID, FQ_E_SHAPE, FQ_E_UNSUPPORTED, FQ_E_WORKSPACE, FQ_E_ALIGN, FQ_E_HIP = 0, -1, -2, -3, -4, -5, -6
