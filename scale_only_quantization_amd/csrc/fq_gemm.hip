@@ -41,7 +41,7 @@
 #endif
 #ifndef GEMM_WVM
 #define GEMM_WVM 2          // waves of the large tile along rows x columns
-#define GEMM_WVN 2
+#define GEMM_WVN 4
 #endif
 #ifndef GEMM_SCHED
 #define GEMM_SCHED 1        // interleave fragment reads with MFMAs explicitly
