@@ -71,8 +71,11 @@ def stage_work(L, fmt):
         "fc1_wgrad": ("mfma", 2.0 * R * 2 * I * H),
         "unpermute_a1": ("hbm", 2 * T * H * bf + R * H * bf),
         "a1_sum": ("hbm", R * 4),
-        "w1_scale_grad": ("hbm", W1 + 2 * W1 + 2 * sw1),
-        "w2_scale_grad": ("hbm", W2 + 2 * W2 + 2 * sw2),
+        # the weight-scale gradients: formed in the weight-gradient GEMM's
+        # epilogue for nvfp4 (nothing left for this stage), else summed from
+        # its per-32-column partials (INT/FP8 per-row, per-group and per-tensor)
+        "w1_scale_grad": ("hbm", 0 if nv else W1 // 2 * 4 // 32 + sw1),
+        "w2_scale_grad": ("hbm", 0 if nv else W2 // 2 * 4 // 32 + sw2),
     }
     return fwd, bwd
 
@@ -108,7 +111,8 @@ KERNELS = {
     "gemm_dgrad": (("fc2_dgrad", "fc1_dgrad"), ("fq_gemm.hip",)),
     "gemm_wgrad": (("fc2_wgrad", "fc1_wgrad"), ("fq_gemm.hip",)),
     "tensor_fwd": (("w1_fq", "w2_fq"), ("fq_tensor.hip",)),
-    "tensor_bwd": (("w1_scale_grad", "w2_scale_grad"), ("fq_tensor.hip",)),
+    # nvfp4: nothing (formed in gemm_wgrad's epilogue); INT/FP8: sums of its partials
+    "weight_scale_grad": (("w1_scale_grad", "w2_scale_grad"), ("fq_gemm.hip", "fq_tensor.hip")),
     "route": (("route",), ("fq_layer.hip",)),
     "permute_a1": (("permute_a1",), ("fq_layer.hip",)),
     "swiglu_a2": (("swiglu_a2",), ("fq_layer.hip",)),

@@ -259,9 +259,15 @@ typedef enum {
     FQ_BUF_DHHAT = 101,  /* bf16 [T*topk, I]                                   */
     FQ_BUF_DZ1 = 102,    /* bf16 [T*topk, 2I]                                  */
     FQ_BUF_DXHAT = 103,  /* bf16 [T*topk, H]                                   */
-    FQ_BUF_DW1HAT = 104, /* fp32 [E, 2I, H]                                    */
-    FQ_BUF_DW2HAT = 105  /* fp32 [E, H, I]                                     */
+    FQ_BUF_DW1HAT = 104, /* fp32 [E, 2I, H]; 0 bytes where ds_w1 is formed in the GEMM */
+    FQ_BUF_DW2HAT = 105  /* fp32 [E, H, I];  0 bytes where ds_w2 is formed in the GEMM */
 } fq_buffer;
+/* The weight gradient dW^ is an intermediate of the weight-scale gradient only
+ * (the weights are frozen).  For learnable NVFP4 weights and for learnable or
+ * static INT/FP8 weights with per-tensor, per-row or per-group (16 or >= 32)
+ * scales, the scale gradient is reduced in the weight-gradient GEMM's epilogue
+ * and dW^ never reaches memory; otherwise (dynamic sources, group 8) it is
+ * stored and reduced by the fake-quant backward. */
 int fq_grouped_expert_buffer(const fq_layer_desc* L, int32_t which, size_t* offset, size_t* bytes);
 
 /* ---- diagnostics ----------------------------------------------------------- */

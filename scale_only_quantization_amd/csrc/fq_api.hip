@@ -92,7 +92,7 @@ struct Layout {
     Section w1hat, w2hat, xhat, z1, hhat, yr;
     size_t saved = 0;
     // workspace
-    Section hist, local_rank, dyr, dhh, dz1, dxh, dw1, dw2, rowpart1, rowpart2, tws;
+    Section hist, local_rank, dyr, dhh, dz1, dxh, dw1, dw2, sgp1, sgp2, rowpart1, rowpart2, tws;
     size_t ws = 0;
 };
 
@@ -164,8 +164,13 @@ Layout layout(const fq_layer_desc* L, const LayerQ& q) {
     place(y.dhh, (size_t)R * I * 2, c);
     place(y.dz1, (size_t)R * 2 * I * 2, c);
     place(y.dxh, (size_t)R * H * 2, c);
-    place(y.dw1, q.w1.kind != FQ_NONE ? (size_t)E * 2 * I * H * 4 : 0, c);
-    place(y.dw2, q.w2.kind != FQ_NONE ? (size_t)E * H * I * 4 : 0, c);
+    // dW^ is stored only where the weight-scale gradient is not formed in the
+    // weight-gradient GEMM's epilogue; per-32-column partials where it is
+    const int m1 = sg_mode(q.w1), m2 = sg_mode(q.w2);
+    place(y.dw1, q.w1.kind != FQ_NONE && m1 == 0 ? (size_t)E * 2 * I * H * 4 : 0, c);
+    place(y.dw2, q.w2.kind != FQ_NONE && m2 == 0 ? (size_t)E * H * I * 4 : 0, c);
+    place(y.sgp1, m1 == 2 ? (size_t)E * 2 * I * (H / 32) * 4 : 0, c);
+    place(y.sgp2, m2 == 2 ? (size_t)E * H * (I / 32) * 4 : 0, c);
     place(y.rowpart1, R * 4, c);
     place(y.rowpart2, R * 4, c);
     const size_t t1 = tensor_workspace_bytes(q.w1, E, 2 * I);
@@ -545,6 +550,21 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
     uint16_t* dxh = at<uint16_t>(workspace, lay.dxh);
     float* dw1 = at<float>(workspace, lay.dw1);
     float* dw2 = at<float>(workspace, lay.dw2);
+    const int m1 = sg_mode(q.w1), m2 = sg_mode(q.w2);
+    // the fused weight-scale gradient of one stack: W, its scales, and where
+    // the epilogue writes (the gradient itself, or partials)
+    auto sg_of = [&](const QParams& qq, int m, const void* W, const float* sc, const float* ts, float* ds,
+                     const Section& part) {
+        SgArgs a{};
+        if (m == 0 || !ds) return a;
+        a.q = qq;
+        a.W = static_cast<const uint16_t*>(W);
+        a.scale = sc;
+        a.tscale = ts;
+        a.part32 = m == 2;
+        a.out = m == 2 ? at<float>(workspace, part) : ds;
+        return a;
+    };
 
     // B1: permute dY (and the routing-weight gradient)
     PermuteDyArgs pd{};
@@ -596,7 +616,9 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         g.strideC = (int64_t)H * I;
         g.N = H;
         g.K = I;
+        g.sg = sg_of(q.w2, m2, P->w2, P->s_w2, P->t_w2, G->ds_w2, lay.sgp2);
         FQ_TRY(launch_gemm_wgrad(g, st));
+        g.sg = SgArgs{};
     }
 
     // B4: A2 straight-through + SwiGLU backward
@@ -643,7 +665,9 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         g.strideC = (int64_t)2 * I * H;
         g.N = 2 * I;
         g.K = H;
+        g.sg = sg_of(q.w1, m1, P->w1, P->s_w1, P->t_w1, G->ds_w1, lay.sgp1);
         FQ_TRY(launch_gemm_wgrad(g, st));
+        g.sg = SgArgs{};
     }
     FQ_TRY(mark(events, 7, st));
     if (need_dxh) {
@@ -666,9 +690,13 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
     }
 
     if (!need_dxh) FQ_TRY(mark(events, 8, st));
-    // B8: weight-scale gradients from (W, dW^)
+    // B8: weight-scale gradients; formed in the GEMM epilogue (mode 1), summed
+    // from its partials (mode 2), or from (W, dW^) by the fake-quant backward
     FQ_TRY(mark(events, 9, st));
-    if (G->ds_w1) {
+    if (G->ds_w1 && m1 == 2)
+        FQ_TRY(launch_sg_reduce(q.w1, at<float>(workspace, lay.sgp1), E, 2 * I, H, at<float>(workspace, lay.tws),
+                                G->ds_w1, st));
+    if (G->ds_w1 && m1 == 0) {
         TensorArgs ta{};
         ta.q = q.w1;
         ta.batch = E;
@@ -684,7 +712,10 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         FQ_TRY(launch_tensor_bwd(ta, st));
     }
     FQ_TRY(mark(events, 10, st));
-    if (G->ds_w2) {
+    if (G->ds_w2 && m2 == 2)
+        FQ_TRY(launch_sg_reduce(q.w2, at<float>(workspace, lay.sgp2), E, H, I, at<float>(workspace, lay.tws),
+                                G->ds_w2, st));
+    if (G->ds_w2 && m2 == 0) {
         TensorArgs ta{};
         ta.q = q.w2;
         ta.batch = E;

@@ -172,6 +172,98 @@ __device__ __forceinline__ int xcd_tile(int id, int grid, int tiles) {
     return (id / 8 < chunk && t < tiles) ? t : -1;
 }
 
+template <int KIND>
+__device__ __forceinline__ float sg_part4(const float* w4, const float* g4, const Div& dv, float qmin,
+                                          float qmax) {
+    float part = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const Elem el = quant_elem<KIND>(w4[v], dv, qmin, qmax);
+        part = __builtin_fmaf(g4[v], ste_c(el, qmin, qmax), part);
+    }
+    return part;
+}
+
+// Weight-gradient epilogue with the weight-scale gradient fused: the wave's
+// accumulators are dW_e[i, j] for rows i = i_w + 32 ti + lane%32 and columns
+// j = j_w + 32 tj + 8 q + 4 (lane/32) + v.  Each element's straight-through
+// term c is recomputed from the frozen weight and its effective scale exactly
+// as the fake-quant backward does, and g c is summed per 16-column block
+// (a block is q = 2b, 2b+1 of both lane halves) or per 32-column tile.
+template <int KIND, int WTM, int WTN>
+__device__ __forceinline__ void sg_epilogue(const GemmArgs& g, const f32x16 (&acc)[WTM][WTN], int e,
+                                            int i_w, int j_w, int lane) {
+    const SgArgs& sg = g.sg;
+    const int64_t N = g.N, K = g.K;
+    const float qmin = sg.q.qmin, qmax = sg.q.qmax;
+    const int gran = sg.q.gran, group = sg.q.group;
+    const float t = KIND == K_NVFP4 ? sg.tscale[e] : 0.0f;
+    // weights and scales of 32-row slice ti are fetched while slice ti-1 is
+    // reduced: one memory round trip per slice instead of one per element group
+    uint2 wv[2][WTN][4];
+    float sv[2][WTN][2];
+    auto fetch = [&](int ti, int buf) {
+        const int64_t wrow = (int64_t)e * N + i_w + ti * 32 + (lane & 31);
+        const uint16_t* Wr = sg.W + wrow * K;
+#pragma unroll
+        for (int tj = 0; tj < WTN; ++tj) {
+            const int jt = j_w + tj * 32;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                wv[buf][tj][q] = *reinterpret_cast<const uint2*>(Wr + jt + 8 * q + 4 * (lane >> 5));
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int j = jt + 16 * b;
+                if (KIND == K_NVFP4) sv[buf][tj][b] = sg.scale[wrow * (K >> 4) + (j >> 4)];
+                else if (gran == G_GROUP) sv[buf][tj][b] = sg.scale[wrow * (K / group) + j / group];
+                else if (gran == G_ROW) sv[buf][tj][b] = sg.scale[wrow];
+                else sv[buf][tj][b] = sg.scale[e];
+            }
+        }
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int ti = 0; ti < WTM; ++ti) {
+        const int cur = ti & 1;
+        if (ti + 1 < WTM) fetch(ti + 1, cur ^ 1);
+        const int64_t wrow = (int64_t)e * N + i_w + ti * 32 + (lane & 31);
+#pragma unroll
+        for (int tj = 0; tj < WTN; ++tj) {
+            const int jt = j_w + tj * 32;
+            float p[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                // effective scale of the 16-column block (the block's columns
+                // share one scale for every granularity allowed here)
+                float s = sv[cur][tj][b];
+                if (KIND == K_NVFP4) s = t * e4m3_round(fminf(s / t, 448.0f));
+                Div dv;
+                dv.set(s);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int q = 2 * b + h;
+                    const uint2 w = wv[cur][tj][q];
+                    const float w4[4] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
+                    const float g4[4] = {acc[ti][tj][4 * q], acc[ti][tj][4 * q + 1], acc[ti][tj][4 * q + 2],
+                                         acc[ti][tj][4 * q + 3]};
+                    p[b] += sg_part4<KIND>(w4, g4, dv, qmin, qmax);
+                }
+            }
+            const float b0 = p[0] + __shfl_xor(p[0], 32);
+            const float b1 = p[1] + __shfl_xor(p[1], 32);
+            if (lane < 32) {
+                if (!sg.part32) {
+                    float* o = sg.out + wrow * (K >> 4) + (jt >> 4);   // 4-byte aligned only
+                    o[0] = b0;
+                    o[1] = b1;
+                } else {
+                    sg.out[wrow * (K >> 5) + (jt >> 5)] = b0 + b1;
+                }
+            }
+        }
+    }
+}
+
 template <int MODE, int WVM, int WVN, int WTM, int WTN, int BK, int S>
 __global__ __launch_bounds__(64 * WVM * WVN) void k_gemm(GemmArgs g) {
     constexpr int NW = WVM * WVN;
@@ -306,6 +398,15 @@ __global__ __launch_bounds__(64 * WVM * WVN) void k_gemm(GemmArgs g) {
         compute(stage(kt));
     }
 
+    if constexpr (MODE == WGRAD) {
+        if (g.sg.out) {
+            const int iw = i0 + wm * 32 * WTM, jw = n0 + wn * 32 * WTN;
+            if (g.sg.q.kind == K_NVFP4) sg_epilogue<K_NVFP4, WTM, WTN>(g, acc, e, iw, jw, lane);
+            else if (g.sg.q.kind == K_INT) sg_epilogue<K_INT, WTM, WTN>(g, acc, e, iw, jw, lane);
+            else sg_epilogue<K_FP8, WTM, WTN>(g, acc, e, iw, jw, lane);
+            return;
+        }
+    }
     // epilogue: lane holds C[m = lane%32][n = 8*(v/4) + 4*(lane/32) + v%4] of each 32x32 tile
 #pragma unroll
     for (int ti = 0; ti < WTM; ++ti) {
@@ -375,7 +476,57 @@ hipError_t launch(const GemmArgs& g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// out[o] = sum of `per` consecutive partials (fixed order), o < n_out
+__global__ __launch_bounds__(256) void k_sg_sum(const float* part, int64_t n_out, int per, float* out) {
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (o >= n_out) return;
+    const float* p = part + o * per;
+    float acc = 0.0f;
+    for (int i = 0; i < per; ++i) acc += p[i];
+    out[o] = acc;
+}
+
+// out[b] = sum over rows of in[b, :] (per-matrix gradient), fixed order
+__global__ __launch_bounds__(256) void k_sg_batch(const float* in, int64_t rows, float* out) {
+    __shared__ float red[256];
+    const int64_t b = blockIdx.x;
+    float acc = 0.0f;
+    for (int64_t r = threadIdx.x; r < rows; r += 256) acc += in[b * rows + r];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[b] = red[0];
+}
+
 }  // namespace
+
+int sg_mode(const QParams& q) {
+    if (q.kind == K_NONE || q.source == S_DYNAMIC) return 0;
+    if (q.kind == K_NVFP4) return 1;
+    if (q.gran == G_GROUP) return q.group == 16 ? 1 : (q.group >= 32 ? 2 : 0);
+    return 2;
+}
+
+hipError_t launch_sg_reduce(const QParams& q, const float* part, int64_t E, int64_t N, int64_t K,
+                            float* rowpart, float* out, hipStream_t st) {
+    const int64_t rows = E * N, np = K / 32;
+    if (q.gran == G_GROUP) {
+        const int64_t n_out = rows * (K / q.group);
+        hipLaunchKernelGGL(k_sg_sum, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, st, part, n_out,
+                           q.group / 32, out);
+    } else if (q.gran == G_ROW) {
+        hipLaunchKernelGGL(k_sg_sum, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, part, rows,
+                           (int)np, out);
+    } else {
+        hipLaunchKernelGGL(k_sg_sum, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, part, rows,
+                           (int)np, rowpart);
+        hipLaunchKernelGGL(k_sg_batch, dim3((unsigned)E), dim3(256), 0, st, rowpart, N, out);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm_fwd(const GemmArgs& g, hipStream_t st) { return launch<FWD>(g, st); }
 hipError_t launch_gemm_dgrad(const GemmArgs& g, hipStream_t st) { return launch<DGRAD>(g, st); }

@@ -142,6 +142,25 @@ hipError_t launch_segment_sum(const float* rowpart, const int32_t* offsets, int 
                               float* out, hipStream_t st);
 
 // ------------------------------------------------------------------ GEMMs ---
+// Weight-scale gradient formed in the weight-gradient GEMM's epilogue: for each
+// element of dW_e (never stored) recompute c from the frozen weight and its
+// scale and reduce g c over the scale's elements.
+struct SgArgs {
+    QParams q;
+    const uint16_t* W;     // [E, N, K] frozen weights of the stack
+    const float* scale;    // its scale parameter (NVFP4 block / group / row / tensor)
+    const float* tscale;   // NVFP4 tensor scale [E]
+    float* out;            // null: store dW instead; else per-16 block gradients
+                           // (part32 == 0) or per-32-column partials [E, N, K/32]
+    int part32;
+};
+// How the weight-scale gradient of a quantiser is formed: 0 from a stored dW by
+// the fake-quant backward, 1 directly per 16-column block in the epilogue,
+// 2 from per-32-column partials of the epilogue.
+int sg_mode(const QParams& q);
+hipError_t launch_sg_reduce(const QParams& q, const float* part, int64_t E, int64_t N, int64_t K,
+                            float* rowpart, float* out, hipStream_t st);
+
 // C = A B^T per expert over the routed rows (forward), A K-contiguous, B [N, K].
 struct GemmArgs {
     const uint16_t* A;
@@ -158,6 +177,7 @@ struct GemmArgs {
     const int32_t* tile_row0;
     const int32_t* num_tiles;
     const int32_t* order;
+    SgArgs sg;                    // WGRAD only
 };
 hipError_t launch_gemm_fwd(const GemmArgs& g, hipStream_t st);    // B K-contiguous
 hipError_t launch_gemm_dgrad(const GemmArgs& g, hipStream_t st);  // B N-contiguous ([K, N])

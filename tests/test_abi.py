@@ -108,7 +108,11 @@ def test_layer_sizes_and_buffers():
     assert sz["xhat"][1] == R * 2048 * 2
     assert sz["z1"][1] == R * 1536 * 2
     assert sz["w1hat"][1] == 128 * 1536 * 2048 * 2
-    assert sz["dw1hat"][1] == 128 * 1536 * 2048 * 4
+    assert sz["dw1hat"][1] == 0              # nvfp4: the weight-scale gradient is formed in the GEMM
+    assert F.buffer(_layer("nvfp4a16"), "dw1hat")[1] == 0
+    w1, w2, a1, a2 = F.preset("nvfp4")
+    nv_dyn = F.qdesc(F.FQ_NVFP4, F.FQ_PER_GROUP, 16, F.FQ_DYNAMIC)
+    assert F.buffer(F.layer_desc(128, 2048, 768, 16384, 8, nv_dyn, w2, a1, a2), "dw1hat")[1] == 128 * 1536 * 2048 * 4
     saved = [(o, b) for n, (o, b) in sz.items() if F.BUFFERS[n] < 100]
     work = [(o, b) for n, (o, b) in sz.items() if F.BUFFERS[n] >= 100]
     for group, total in ((saved, F.saved_size(L)), (work, F.workspace_size(L))):

@@ -59,8 +59,10 @@ def _full_parity(L, data, P, Po, end_to_end=True):
     W1h, W2h = w1t["y"], w2t["y"]
     Xh, Z1, Hh, Yr = dl.read("xhat"), dl.read("z1"), dl.read("hhat"), dl.read("yr")
     dYr, dHh, dZ1, dXh = dl.read("dyr"), dl.read("dhhat"), dl.read("dz1"), dl.read("dxhat")
-    dW1 = dl.read("dw1hat") if L.w1.enabled else None
-    dW2 = dl.read("dw2hat") if L.w2.enabled else None
+    # dW^ reaches memory only where the weight-scale gradient is not formed in
+    # the weight-gradient GEMM's epilogue
+    dW1 = dl.read("dw1hat") if L.w1.enabled and dl.F.buffer(dl.desc, "dw1hat")[1] else None
+    dW2 = dl.read("dw2hat") if L.w2.enabled and dl.F.buffer(dl.desc, "dw2hat")[1] else None
     sa1, sa2 = P.get("s_a1"), P.get("s_a2")
     ds_a1_ref = np.zeros(L.E)
     ds_a2_ref = np.zeros(L.E)
@@ -139,13 +141,27 @@ def _full_parity(L, data, P, Po, end_to_end=True):
         check_scale_grad(_g(dl, "ds_a1"), ds_a1_ref, g1, "ds_a1")
     if dl.g["ds_a2"] is not None:
         check_scale_grad(_g(dl, "ds_a2"), ds_a2_ref, g2, "ds_a2")
-    # weight-scale gradients from the device's dW^ (stage-wise)
-    for n, q, W, dW, terms, s, t in (("ds_w1", L.w1, data["W1"], dW1, w1t, P.get("s_w1"), P.get("t_w1")),
-                                     ("ds_w2", L.w2, data["W2"], dW2, w2t, P.get("s_w2"), P.get("t_w2"))):
+    # weight-scale gradients (stage-wise): from the device's dW^ where it is
+    # stored; else from dW^ of the device's GEMM operands in float64, where the
+    # device accumulated dW^ in fp32 over each expert's rows, so the cancellation
+    # guard takes |dW^| <= |A|^T |B|
+    for n, q, W, dW, terms, s, t, A, B in (
+            ("ds_w1", L.w1, data["W1"], dW1, w1t, P.get("s_w1"), P.get("t_w1"), dZ1, Xh),
+            ("ds_w2", L.w2, data["W2"], dW2, w2t, P.get("s_w2"), P.get("t_w2"), dYr, Hh)):
         if dl.g[n] is None:
             continue
-        _, ref = codec.backward(q, W, dW.astype(np.float64), s, t, terms=terms)
-        check_scale_grad(_g(dl, n), ref, _guard(q, W, dW, terms), n)
+        if dW is not None:
+            _, ref = codec.backward(q, W, dW.astype(np.float64), s, t, terms=terms)
+            check_scale_grad(_g(dl, n), ref, _guard(q, W, dW, terms), n)
+            continue
+        dWr = np.zeros(W.shape)
+        dWa = np.zeros(W.shape)
+        for e in range(L.E):
+            rows = slice(int(offsets[e]), int(offsets[e + 1]))
+            dWr[e] = OL.gemm_tn(A[rows], B[rows])
+            dWa[e] = OL.gemm_tn(np.abs(A[rows]), np.abs(B[rows]))
+        _, ref = codec.backward(q, W, dWr, s, t, terms=terms)
+        check_scale_grad(_g(dl, n), ref, _guard(q, W, dWa, terms), n)
     if not end_to_end:
         return dl
     # end to end: the oracle's own chain
