@@ -88,11 +88,11 @@ struct Section {
 
 struct Layout {
     // saved
-    Section counts, offsets, row_of, src_of, tile_expert[2], tile_row0[2], num_tiles, order;
+    Section counts, offsets, row_of, src_of, tile_expert[2], tile_row0[2], num_tiles, order, wg_list, wg_cnt;
     Section w1hat, w2hat, xhat, z1, hhat, yr;
     size_t saved = 0;
     // workspace
-    Section hist, local_rank, dyr, dhh, dz1, dxh, dw1, dw2, sgp1, sgp2, rowpart1, rowpart2, tws;
+    Section hist, local_rank, dyr, dhh, dz1, dxh, dw1, dw2, sgp1, sgp2, rowpart1, rowpart2, tws, wg_ctr;
     size_t ws = 0;
 };
 
@@ -150,6 +150,8 @@ Layout layout(const fq_layer_desc* L, const LayerQ& q) {
     }
     place(y.num_tiles, 2 * 4, c);
     place(y.order, E * 4, c);
+    place(y.wg_list, 8 * E * 4, c);
+    place(y.wg_cnt, 8 * 4, c);
     place(y.w1hat, q.w1.kind != FQ_NONE ? (size_t)E * 2 * I * H * 2 : 0, c);
     place(y.w2hat, q.w2.kind != FQ_NONE ? (size_t)E * H * I * 2 : 0, c);
     place(y.xhat, (size_t)R * H * 2, c);
@@ -176,6 +178,7 @@ Layout layout(const fq_layer_desc* L, const LayerQ& q) {
     const size_t t1 = tensor_workspace_bytes(q.w1, E, 2 * I);
     const size_t t2 = tensor_workspace_bytes(q.w2, E, H);
     place(y.tws, t1 > t2 ? t1 : t2, c);
+    place(y.wg_ctr, 16 * 4, c);
     y.ws = c;
     return y;
 }
@@ -396,6 +399,8 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
         ra.tables[h].num_tiles = at<int32_t>(saved, lay.num_tiles) + h;
     }
     ra.order = at<int32_t>(saved, lay.order);
+    ra.wg_list = at<int32_t>(saved, lay.wg_list);
+    ra.wg_cnt = at<int32_t>(saved, lay.wg_cnt);
     ra.hist = at<int32_t>(workspace, lay.hist);
     ra.local_rank = at<int32_t>(workspace, lay.local_rank);
     FQ_TRY(mark(events, 0, st));
@@ -590,6 +595,10 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         g.tables[h].num_tiles = const_cast<int32_t*>(at<int32_t>(saved, lay.num_tiles)) + h;
     }
     g.order = at<int32_t>(saved, lay.order);
+    g.wg_list = at<int32_t>(saved, lay.wg_list);
+    g.wg_cnt = at<int32_t>(saved, lay.wg_cnt);
+    int32_t* wg_ctr = at<int32_t>(workspace, lay.wg_ctr);     // fc2, fc1 weight-gradient tile counters
+    if (G->ds_w1 || G->ds_w2) FQ_TRY(launch_zero_i32(wg_ctr, 16, st));
 
     // B2: fc2 dgrad  dH^ = dY_r W2^
     g.A = dyr;
@@ -617,6 +626,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         g.N = H;
         g.K = I;
         g.sg = sg_of(q.w2, m2, P->w2, P->s_w2, P->t_w2, G->ds_w2, lay.sgp2);
+        g.wg_ctr = wg_ctr;
         FQ_TRY(launch_gemm_wgrad(g, st));
         g.sg = SgArgs{};
     }
@@ -666,6 +676,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         g.N = 2 * I;
         g.K = H;
         g.sg = sg_of(q.w1, m1, P->w1, P->s_w1, P->t_w1, G->ds_w1, lay.sgp1);
+        g.wg_ctr = wg_ctr + 8;
         FQ_TRY(launch_gemm_wgrad(g, st));
         g.sg = SgArgs{};
     }

@@ -6,27 +6,28 @@
 //   DGRAD  C[r, n]    = sum_k A[r, k] B_e[k, n]      B stored [K, N]           (bf16 out)
 //   WGRAD  C_e[i, j]  = sum_r A[r, i] B[r, j]        rows r of expert e        (fp32 out)
 //
-// Block: 256 threads = 4 waves as 2 x 2; each wave owns WTM x WTN 32 x 32
-// output tiles (v_mfma_f32_32x32x16_bf16), so the block tile is
-// (64 WTM) x (64 WTN); with 4 x 4 a wave holds 128 x 128 fp32 accumulators
-// (256 per lane), which keeps LDS reads per MFMA low.
+// Block: WVM x WVN waves; each wave owns WTM x WTN 32 x 32 output tiles
+// (v_mfma_f32_32x32x16_bf16).  Large tile: 256 x 256 on 8 waves (2 x 4, each
+// 128 x 64, two waves per SIMD); small tile: 128 x 128 on 4 waves.
 //
 // Operands go from global memory straight into LDS (buffer_load ... lds,
 // 16 B per lane; one wave instruction fills 1 KB), through buffer resources
 // bounded to the valid rows, so rows past the routed rows or past an expert's
-// rows (the WGRAD reduction tail) read as zero.  A reduction step is 32 deep;
+// rows (the WGRAD reduction tail) read as zero.  A reduction step is BK deep;
 // S LDS stages are in flight, so a tile's loads are issued S-1 steps before
 // its MFMAs.
-//   K-contiguous operand: LDS [rows][32] (64 B per row), the 16-B chunk index
-//     XOR (row >> 1) & 3; a fragment (8 consecutive k of one row) is one
+//   K-contiguous operand: LDS [rows][BK], the 16-B chunk index XORed with a
+//     row swizzle; a fragment (8 consecutive k of one row) is one
 //     ds_read_b128, and 8 consecutive rows at one chunk cover all banks.
-//   Row-contiguous operand: LDS [32][rows] as in memory, the 16-B chunk index
-//     XOR 2 (k & 3); a fragment is two ds_read_b64_tr_b16: inside each group
+//   Row-contiguous operand: LDS [BK][rows] as in memory, the 16-B chunk index
+//     XOR 4 (k & 3), so the 32 lanes of one ds_read_b64_tr_b16 pass (4 k-rows
+//     x 64 B) fall on distinct banks; a fragment is two such reads: inside each group
 //     of 16 lanes, lane i points at k-row kb + i/4, columns mb + 4(i%4) .. +3,
 //     and lane j receives k = kb .. kb+3 of column mb + j.
 // FWD/DGRAD row tiles come from a device-side tile table (expert, first row)
-// built by the routing scan, so no host read-back of the counts is needed;
-// WGRAD visits experts in descending row count.
+// built by the routing scan, so no host read-back of the counts is needed.
+// WGRAD is persistent: each XCD works through its own experts' tiles (an
+// assignment the routing scan balances), taken from a per-XCD counter.
 #include <type_traits>
 
 #include "fq_common.h"
@@ -54,6 +55,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_t;
 
 
@@ -71,15 +73,16 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 // K-contiguous operand tile [ROWS][BK]: element (row, k) at byte row*ld2 + 2k
 // of the resource.  Rows of 2 BK bytes; each 1-KB wave load covers 512/BK rows.
-// Swizzle: chunk ^ (row >> 1) & 3 for 64-B rows, chunk ^ (row ^ row >> 3) & 7
-// for 128-B rows, so 8 consecutive rows at one chunk cover all banks.
+// Swizzle: chunk ^ (row >> 2) & 3 for 64-B rows, chunk ^ (row ^ row >> 3) & 7
+// for 128-B rows, so the 16 rows one ds_read_b128 pass serves (16 lanes x 16 B,
+// 64 banks) fall on distinct banks.
 template <int ROWS, int BK, int NW>
 struct KTile {
     static constexpr int BYTES = ROWS * BK * 2;
     static constexpr int PER_WAVE = BYTES / 1024 / NW;
     static constexpr int CPR = BK / 8;                 // 16-B chunks per row
     __device__ static __forceinline__ int swz(int row) {
-        return BK == 32 ? ((row >> 1) & 3) : ((row ^ (row >> 3)) & 7);
+        return BK == 32 ? ((row >> 2) & 3) : ((row ^ (row >> 3)) & 7);
     }
     __device__ static __forceinline__ int off(int row, int ch) {   // byte offset of 16-B chunk
         return row * (2 * BK) + ((ch ^ swz(row)) << 4);
@@ -121,7 +124,7 @@ struct MNTile {
     static constexpr int PER_WAVE = BYTES / 1024 / NW;
     static constexpr int RB = ROWS * 2;               // bytes per k-row
     __device__ static __forceinline__ int off(int k, int byte) {   // swizzled byte offset
-        return k * RB + (((byte >> 4) ^ ((k & 3) << 1)) << 4) + (byte & 15);
+        return k * RB + (((byte >> 4) ^ ((k & 3) << 2)) << 4) + (byte & 15);
     }
     __amdgpu_buffer_rsrc_t rs;
     uint32_t voff[PER_WAVE];
@@ -135,7 +138,7 @@ struct MNTile {
             const int pos = (NW * i + w) * 1024 + lane * 16;  // byte position in the tile
             const int k = pos / RB;
             const int pc = (pos % RB) >> 4;
-            const int lc = pc ^ ((k & 3) << 1);
+            const int lc = pc ^ ((k & 3) << 2);
             voff[i] = (uint32_t)(k * ld * 2 + lc * 16);
         }
     }
@@ -279,59 +282,20 @@ __global__ __launch_bounds__(64 * WVM * WVN) void k_gemm(GemmArgs g) {
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WVN, wn = wave % WVN;
 
-    int e, nk;
-    int64_t m0 = 0, m_end = 0;      // FWD/DGRAD: routed row range of the tile's expert
-    int n0, i0 = 0;
     ATile la;
     BTile lb;
-
-    if (MODE != WGRAD) {
-        const int ntn = g.N / BN;
-        const int tile = GEMM_XCD ? xcd_tile(blockIdx.x, gridDim.x, g.num_tiles[0] * ntn) : (int)blockIdx.x;
-        if (tile < 0 || tile >= g.num_tiles[0] * ntn) return;
-        const int mt = tile / ntn;
-        const int nt = tile - mt * ntn;
-        e = min(max(g.tile_expert[mt], 0), g.E - 1);
-        m0 = g.tile_row0[mt];
-        m_end = min((int64_t)g.offsets[e + 1], g.R);
-        n0 = nt * BN;
-        nk = g.K / BK;
-        // rows past the routed rows read as zero (their outputs are not stored)
-        la.init(make_rsrc(g.A + m0 * g.lda, (g.R - m0) * g.lda * 2), g.lda);
-        const uint16_t* Be = g.B + (int64_t)e * g.strideB;
-        if constexpr (MODE == FWD)
-            lb.init(make_rsrc(Be + (int64_t)n0 * g.ldb, (int64_t)BN * g.ldb * 2), g.ldb);
-        else
-            lb.init(make_rsrc(Be + n0, ((int64_t)g.K - 1) * g.ldb * 2 + (int64_t)BN * 2), g.ldb);
-    } else {
-        const int tj = g.K / BN;              // output [N, K] per expert
-        const int tpe = (g.N / BM) * tj;
-        // longest reductions first, dealt round-robin over the XCDs
-        const int tile = blockIdx.x;
-        if (tile >= g.E * tpe) return;
-        const int eo = tile / tpe;
-        const int tt = tile - eo * tpe;
-        e = min(max(g.order[eo], 0), g.E - 1);
-        i0 = (tt / tj) * BM;
-        n0 = (tt - (tt / tj) * tj) * BN;
-        const int64_t rb = g.offsets[e];
-        const int me = (int)(min((int64_t)g.offsets[e + 1], g.R) - rb);
-        nk = (me + BK - 1) / BK;
-        // bounded to the expert's rows: the last reduction step's tail reads zeros
-        la.init(make_rsrc(g.A + rb * g.lda + i0, (int64_t)me * g.lda * 2 - i0 * 2), g.lda);
-        lb.init(make_rsrc(g.B + rb * g.ldb + n0, (int64_t)me * g.ldb * 2 - n0 * 2), g.ldb);
-    }
-
     f32x16 acc[WTM][WTN];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int a = 0; a < WTM; ++a)
+        for (int a = 0; a < WTM; ++a)
 #pragma unroll
-        for (int b = 0; b < WTN; ++b)
+            for (int b = 0; b < WTN; ++b)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+                for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+    };
 
-    // MFMAs of one 32-deep step: fragments of the second 16-deep half are
-    // read while the first half's MFMAs run.
+    // MFMAs of one BK-deep step: fragments of the next 16-deep sub-step are
+    // read while the current sub-step's MFMAs run.
     auto compute = [&](const lds_t* st) {
         const lds_t* sa = st;
         const lds_t* sb = st + A_BYTES;
@@ -377,59 +341,151 @@ __global__ __launch_bounds__(64 * WVM * WVN) void k_gemm(GemmArgs g) {
         la.issue(stage(kt), kt * BK);
         lb.issue(stage(kt) + A_BYTES, kt * BK);
     };
-
-    // prologue: S-1 steps in flight
+    // the first S-1 steps in flight
+    auto prologue = [&](int nk) {
 #pragma unroll
-    for (int p = 0; p < S - 1; ++p)
-        if (p < nk) issue(p);
-    for (int kt = 0; kt < nk; ++kt) {
-        // this wave's loads of step kt are done once at most the loads of the
-        // S-2 later steps are outstanding; the barrier then covers every wave
-        if (kt + S - 2 < nk) {
-            if constexpr (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            else if constexpr (S == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int p = 0; p < S - 1; ++p)
+            if (p < nk) issue(p);
+    };
+    auto mainloop = [&](int nk) {
+        for (int kt = 0; kt < nk; ++kt) {
+            // this wave's loads of step kt are done once at most the loads of the
+            // S-2 later steps are outstanding; the barrier then covers every wave
+            if (kt + S - 2 < nk) {
+                if constexpr (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                else if constexpr (S == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+                else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();
+            // the stage step kt+S-1 overwrites was read in step kt-1, finished by every wave
+            if (kt + S - 1 < nk) issue(kt + S - 1);
+            compute(stage(kt));
+        }
+    };
+
+    if constexpr (MODE != WGRAD) {
+        const int ntn = g.N / BN;
+        const int tile = GEMM_XCD ? xcd_tile(blockIdx.x, gridDim.x, g.num_tiles[0] * ntn) : (int)blockIdx.x;
+        if (tile < 0 || tile >= g.num_tiles[0] * ntn) return;
+        const int mt = tile / ntn;
+        const int nt = tile - mt * ntn;
+        const int e = min(max(g.tile_expert[mt], 0), g.E - 1);
+        const int64_t m0 = g.tile_row0[mt];
+        const int64_t m_end = min((int64_t)g.offsets[e + 1], g.R);   // the tile's expert's rows
+        const int n0 = nt * BN;
+        const int nk = g.K / BK;
+        // rows past the routed rows read as zero (their outputs are not stored)
+        la.init(make_rsrc(g.A + m0 * g.lda, (g.R - m0) * g.lda * 2), g.lda);
+        const uint16_t* Be = g.B + (int64_t)e * g.strideB;
+        if constexpr (MODE == FWD)
+            lb.init(make_rsrc(Be + (int64_t)n0 * g.ldb, (int64_t)BN * g.ldb * 2), g.ldb);
+        else
+            lb.init(make_rsrc(Be + n0, ((int64_t)g.K - 1) * g.ldb * 2 + (int64_t)BN * 2), g.ldb);
+        zero_acc();
+        prologue(nk);
+        mainloop(nk);
+        // Epilogue through LDS, so that global stores are whole row segments:
+        // lane holds C[m = lane%32][n = 8*(v/4) + 4*(lane/32) + v%4] of each
+        // 32x32 tile; it is written as bf16 into an LDS tile [BM][BN] whose
+        // 16-B chunks are XOR-swizzled by (row & 15), then each wave copies
+        // two rows per instruction (16 B per lane) to C.
+        constexpr int RB = BN * 2, CH = BN / 8;                 // row bytes, 16-B chunks per row
+        static_assert(BM * RB <= S * STAGE, "C tile fits the LDS stages");
+        __syncthreads();                                         // every wave is done with the stages
+#pragma unroll
+        for (int ti = 0; ti < WTM; ++ti) {
+            const int row = wm * 32 * WTM + ti * 32 + (lane & 31);
+#pragma unroll
+            for (int tj = 0; tj < WTN; ++tj) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = wn * 32 * WTN + tj * 32 + 8 * q + 4 * (lane >> 5);
+                    const int off = row * RB + (((col >> 3) ^ (row & 15)) << 4) + (col & 7) * 2;
+                    *reinterpret_cast<__attribute__((address_space(3))) uint64_t*>(smem + off) =
+                        (uint64_t)pack_bf16(acc[ti][tj][4 * q], acc[ti][tj][4 * q + 1]) |
+                        ((uint64_t)pack_bf16(acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]) << 32);
+                }
+            }
         }
         __syncthreads();
-        // the stage step kt+S-1 overwrites was read in step kt-1, finished by every wave
-        if (kt + S - 1 < nk) issue(kt + S - 1);
-        compute(stage(kt));
-    }
-
-    if constexpr (MODE == WGRAD) {
-        if (g.sg.out) {
-            const int iw = i0 + wm * 32 * WTM, jw = n0 + wn * 32 * WTN;
-            if (g.sg.q.kind == K_NVFP4) sg_epilogue<K_NVFP4, WTM, WTN>(g, acc, e, iw, jw, lane);
-            else if (g.sg.q.kind == K_INT) sg_epilogue<K_INT, WTM, WTN>(g, acc, e, iw, jw, lane);
-            else sg_epilogue<K_FP8, WTM, WTN>(g, acc, e, iw, jw, lane);
-            return;
+        constexpr int RPI = 64 / CH;                             // rows per wave instruction
+#pragma unroll
+        for (int it = 0; it < BM / (RPI * NW); ++it) {
+            const int row = (it * NW + wave) * RPI + lane / CH;
+            const int c = lane % CH;
+            const int64_t r = m0 + row;
+            const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                smem + row * RB + ((c ^ (row & 15)) << 4));
+            if (r < m_end) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.C) + r * g.ldc + n0 + c * 8) = v;
         }
-    }
-    // epilogue: lane holds C[m = lane%32][n = 8*(v/4) + 4*(lane/32) + v%4] of each 32x32 tile
+    } else {
+        // Persistent: the blocks of XCD group x = blockIdx % 8 (dealt to XCD x)
+        // take the tiles of that XCD's experts (longest first) from a counter,
+        // so the tiles sharing an expert's operand rows meet in one L2.  The
+        // next tile's first loads are issued before this tile's epilogue.
+        __shared__ int s_slot;
+        const int x = blockIdx.x & 7;
+        const int tj_n = g.K / BN;                     // output [N, K] per expert
+        const int tpe = (g.N / BM) * tj_n;
+        const int tiles_x = min(max(g.wg_cnt[x], 0), g.E) * tpe;
+        int e = 0, i0 = 0, n0 = 0, nk = 0;
+        auto setup = [&](int slot) {
+            const int eo = slot / tpe;
+            const int tt = slot - eo * tpe;
+            e = min(max(g.wg_list[x * g.E + eo], 0), g.E - 1);
+            i0 = (tt / tj_n) * BM;
+            n0 = (tt - (tt / tj_n) * tj_n) * BN;
+            const int64_t rb = g.offsets[e];
+            const int me = (int)(min((int64_t)g.offsets[e + 1], g.R) - rb);
+            nk = (me + BK - 1) / BK;
+            // bounded to the expert's rows: the last reduction step's tail reads zeros
+            la.init(make_rsrc(g.A + rb * g.lda + i0, (int64_t)me * g.lda * 2 - i0 * 2), g.lda);
+            lb.init(make_rsrc(g.B + rb * g.ldb + n0, (int64_t)me * g.ldb * 2 - n0 * 2), g.ldb);
+        };
+        if (threadIdx.x == 0) s_slot = atomicAdd(g.wg_ctr + x, 1);
+        __syncthreads();
+        int slot = s_slot;
+        if (slot < 0 || slot >= tiles_x) return;
+        setup(slot);
+        prologue(nk);
+        for (;;) {
+            zero_acc();
+            mainloop(nk);
+            __syncthreads();          // LDS stages free; every wave has read s_slot
+            if (threadIdx.x == 0) s_slot = atomicAdd(g.wg_ctr + x, 1);
+            __syncthreads();
+            const int next = s_slot;
+            const int ce = e, ci0 = i0, cn0 = n0;
+            const bool more = next >= 0 && next < tiles_x;
+            if (more) {
+                setup(next);
+                prologue(nk);
+            }
+            if (g.sg.out) {
+                const int iw = ci0 + wm * 32 * WTM, jw = cn0 + wn * 32 * WTN;
+                if (g.sg.q.kind == K_NVFP4) sg_epilogue<K_NVFP4, WTM, WTN>(g, acc, ce, iw, jw, lane);
+                else if (g.sg.q.kind == K_INT) sg_epilogue<K_INT, WTM, WTN>(g, acc, ce, iw, jw, lane);
+                else sg_epilogue<K_FP8, WTM, WTN>(g, acc, ce, iw, jw, lane);
+            } else {
 #pragma unroll
-    for (int ti = 0; ti < WTM; ++ti) {
-        const int ml = wm * 32 * WTM + ti * 32 + (lane & 31);
+                for (int ti = 0; ti < WTM; ++ti) {
+                    const int ml = wm * 32 * WTM + ti * 32 + (lane & 31);
 #pragma unroll
-        for (int tj = 0; tj < WTN; ++tj) {
+                    for (int tj = 0; tj < WTN; ++tj) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int nl = wn * 32 * WTN + tj * 32 + 8 * q + 4 * (lane >> 5);
-                const float c0 = acc[ti][tj][4 * q], c1 = acc[ti][tj][4 * q + 1];
-                const float c2 = acc[ti][tj][4 * q + 2], c3 = acc[ti][tj][4 * q + 3];
-                if (MODE == WGRAD) {
-                    float* C = static_cast<float*>(g.C) + (int64_t)e * g.strideC +
-                               (int64_t)(i0 + ml) * g.ldc + n0 + nl;
-                    *reinterpret_cast<float4*>(C) = make_float4(c0, c1, c2, c3);
-                } else {
-                    const int64_t r = m0 + ml;
-                    if (r < m_end) {
-                        uint16_t* C = static_cast<uint16_t*>(g.C) + r * g.ldc + n0 + nl;
-                        *reinterpret_cast<uint2*>(C) = make_uint2(pack_bf16(c0, c1), pack_bf16(c2, c3));
+                        for (int q = 0; q < 4; ++q) {
+                            const int nl = wn * 32 * WTN + tj * 32 + 8 * q + 4 * (lane >> 5);
+                            float* C = static_cast<float*>(g.C) + (int64_t)ce * g.strideC +
+                                       (int64_t)(ci0 + ml) * g.ldc + cn0 + nl;
+                            *reinterpret_cast<float4*>(C) = make_float4(acc[ti][tj][4 * q], acc[ti][tj][4 * q + 1],
+                                                                        acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
+                        }
                     }
                 }
             }
+            if (!more) break;
         }
     }
 }
@@ -467,8 +523,13 @@ hipError_t launch(const GemmArgs& g, hipStream_t st) {
         const int bm = big ? 256 : 128;
         blocks = max_mtiles(g.R, g.E, bm) * (g.N / bm);
     } else {
-        const int t = big ? 256 : 128;
-        blocks = (int64_t)g.E * (g.N / t) * (g.K / t);
+        // persistent: as many blocks as fit on the device at once (LDS bound:
+        // one large-tile block or two small-tile blocks per CU), 8 groups
+        int dev = 0, cus = 0;
+        hipError_t err = hipGetDevice(&dev);
+        if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return err;
+        blocks = (int64_t)(cus > 8 ? cus : 8) * (big ? 1 : 2);
     }
     blocks = (blocks + 7) / 8 * 8;       // a whole number of blocks per XCD
     if (big) hipLaunchKernelGGL((FQ_BIG(MODE)), dim3((unsigned)blocks), dim3(64 * WVM_BIG * WVN_BIG), 0, st, a);
@@ -501,7 +562,16 @@ __global__ __launch_bounds__(256) void k_sg_batch(const float* in, int64_t rows,
     if (threadIdx.x == 0) out[b] = red[0];
 }
 
+__global__ void k_zero_i32(int32_t* p, int n) {
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st) {
+    hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, st, p, n);
+    return hipGetLastError();
+}
 
 int sg_mode(const QParams& q) {
     if (q.kind == K_NONE || q.source == S_DYNAMIC) return 0;

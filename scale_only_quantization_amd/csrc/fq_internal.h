@@ -54,6 +54,8 @@ struct RouteArgs {
     int32_t* src_of;       // [R]
     TileTable tables[2];   // heights 128 and 256
     int32_t* order;        // [E] experts by descending count
+    int32_t* wg_list;      // [8, E] experts of each XCD's weight-gradient work, descending
+    int32_t* wg_cnt;       // [8] experts per XCD
     int32_t* hist;         // workspace [nblk, E]
     int32_t* local_rank;   // workspace [R]
 };
@@ -178,9 +180,13 @@ struct GemmArgs {
     const int32_t* num_tiles;
     const int32_t* order;
     SgArgs sg;                    // WGRAD only
+    const int32_t* wg_list;       // WGRAD: [8, E] experts per XCD (routing scan)
+    const int32_t* wg_cnt;        // [8]
+    int32_t* wg_ctr;              // [8] tile counters, zero at launch
 };
 hipError_t launch_gemm_fwd(const GemmArgs& g, hipStream_t st);    // B K-contiguous
 hipError_t launch_gemm_dgrad(const GemmArgs& g, hipStream_t st);  // B N-contiguous ([K, N])
 hipError_t launch_gemm_wgrad(const GemmArgs& g, hipStream_t st);  // C[e] fp32 [N, K] = A_e^T B_e
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);
 
 }  // namespace fq

@@ -81,8 +81,9 @@ __global__ __launch_bounds__(TPB) void k_route_local(const int32_t* ids, int64_t
 // (ties by id).
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, int E, int32_t* counts,
                                                      int32_t* offsets, TileTable t128, TileTable t256,
-                                                     int32_t* order) {
+                                                     int32_t* order, int32_t* wg_list, int32_t* wg_cnt) {
     __shared__ int32_t s_cnt[1024];
+    __shared__ int32_t s_ord[1024];
     __shared__ int32_t s_a[1024];
     __shared__ int32_t s_b[1024];
     __shared__ int32_t s_c[1024];
@@ -137,7 +138,30 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
             rank += (c > cnt) || (c == cnt && o < e);
         }
         order[rank] = e;
+        s_ord[rank] = e;
         for (int b = 0; b < nblk; ++b) hist[(int64_t)b * E + e] += off;
+    }
+    __syncthreads();
+    // Weight-gradient work per XCD (each XCD has its own L2): experts in
+    // descending count go to the least loaded XCD so far (ties: lowest XCD),
+    // load = reduction steps of 64 rows + 2 for the epilogue.  One wave; lane
+    // x < 8 keeps XCD x's load and list.
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int load = 0, n = 0;
+        for (int r = 0; r < E; ++r) {
+            const int ex = s_ord[r];
+            int key = lane < 8 ? load * 8 + lane : 0x7FFFFFFF;
+            key = min(key, __shfl_xor(key, 1));
+            key = min(key, __shfl_xor(key, 2));
+            key = min(key, __shfl_xor(key, 4));
+            if (lane == (key & 7)) {
+                wg_list[lane * E + n] = ex;
+                ++n;
+                load += (s_cnt[ex] + 63) / 64 + 2;
+            }
+        }
+        if (lane < 8) wg_cnt[lane] = n;
     }
 }
 
@@ -604,7 +628,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
         if (err != hipSuccess) return err;
     }
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, a.hist, (int)nblk, a.E, a.counts,
-                       a.offsets, a.tables[0], a.tables[1], a.order);
+                       a.offsets, a.tables[0], a.tables[1], a.order, a.wg_list, a.wg_cnt);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nblk == 0) return err;
     hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nblk), dim3(TPB), 0, st, a.ids, a.R, a.E, a.hist,
