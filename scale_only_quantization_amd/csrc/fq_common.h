@@ -66,21 +66,22 @@ __device__ __forceinline__ float group_sum(float v, int lanes) {
 
 // ----------------------------------------------------------------- grids ---
 // E4M3FN round-to-nearest-even of a magnitude in [0, 448] (callers saturate
-// first).  Returns the value; *code gets the 7-bit magnitude code.
+// first).  Returns the value; *code gets the 7-bit magnitude code.  Both the
+// subnormal (spacing 2^-9 below 2^-6) and the normal rounding are formed and
+// one is selected, so lanes never diverge.
 __device__ __forceinline__ float e4m3_round(float a, uint32_t* code) {
-    if (a < 0.015625f) {                       // below 2^-6: subnormal spacing 2^-9
-        float m = rintf(a * 512.0f);           // exact scaling, ties to even
-        *code = (uint32_t)m;                   // 0..8 (8 == 2^-6, code 0x08)
-        return m * 0.001953125f;
-    }
+    const float m = rintf(a * 512.0f);                 // exact scaling, ties to even
     uint32_t u = __float_as_uint(a);
     u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;   // keep 3 mantissa bits
-    *code = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
-    return __uint_as_float(u);
+    const bool sub = a < 0.015625f;
+    *code = sub ? (uint32_t)m : ((((u >> 23) - 120u) << 3) | ((u >> 20) & 7u));   // 8 == 2^-6, code 0x08
+    return sub ? m * 0.001953125f : __uint_as_float(u);
 }
 __device__ __forceinline__ float e4m3_round(float a) {
-    uint32_t c;
-    return e4m3_round(a, &c);
+    const float m = rintf(a * 512.0f);
+    uint32_t u = __float_as_uint(a);
+    u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
+    return a < 0.015625f ? m * 0.001953125f : __uint_as_float(u);
 }
 
 // E2M1 round-to-nearest-even of a magnitude in [0, 6]: spacing 0.5 below 2,
@@ -125,6 +126,14 @@ struct Elem {
     bool inside;
 };
 
+// grid value of r (sign of x), r already divided
+template <int KIND>
+__device__ __forceinline__ float grid_q(float r, float x, float qmin, float qmax) {
+    if (KIND == K_INT) return copysignf(rintf(fminf(fmaxf(r, qmin), qmax)), x);   // sign from x:
+    if (KIND == K_NVFP4) return copysignf(e2m1_round(fminf(fabsf(r), 6.0f)), x);    // the corrected
+    return copysignf(e4m3_round(fminf(fabsf(r), 448.0f)), x);                        // division gives +0 for -0
+}
+
 template <int KIND>
 __device__ __forceinline__ Elem quant_elem(float x, const Div& d, float qmin, float qmax) {
     Elem e;
@@ -134,20 +143,41 @@ __device__ __forceinline__ Elem quant_elem(float x, const Div& d, float qmin, fl
         e.inside = true;
         return e;
     }
-    float r = d(x);
+    const float r = d(x);
     e.r = r;
     e.inside = (r >= qmin) && (r <= qmax);
-    if (KIND == K_INT) {
-        // the sign comes from x (the corrected division returns +0 for x = -0)
-        e.q = copysignf(rintf(fminf(fmaxf(r, qmin), qmax)), x);
-    } else if (KIND == K_NVFP4) {
-        float a = fminf(fabsf(r), 6.0f);
-        e.q = copysignf(e2m1_round(a), x);
-    } else {
-        float a = fminf(fabsf(r), 448.0f);
-        e.q = copysignf(e4m3_round(a), x);
-    }
+    e.q = grid_q<KIND>(r, x, qmin, qmax);
     return e;
+}
+
+// quant_elem for a scale known to be in the normal range [2^-120, 2^120]:
+// no zero case and the corrected division only, so no branches
+template <int KIND>
+__device__ __forceinline__ Elem quant_fast(float x, const Div& d, float qmin, float qmax) {
+    const float q0 = x * d.inv;
+    const float rem = __builtin_fmaf(-q0, d.s, x);
+    const float r = __builtin_fmaf(rem, d.inv, q0);
+    Elem e;
+    e.r = r;
+    e.inside = (r >= qmin) && (r <= qmax);
+    e.q = grid_q<KIND>(r, x, qmin, qmax);
+    return e;
+}
+
+// Run f(i, Elem) over the N elements x[0..N) sharing the effective scale s.
+// The wave takes the branch-free path when every active lane's scale is in
+// the normal range (a wave-uniform branch), else the general one.
+template <int KIND, int N, typename F>
+__device__ __forceinline__ void quant_group(const float* x, float s, float qmin, float qmax, F&& f) {
+    Div dv;
+    dv.set(s);
+    if (__all(dv.fast)) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) f(i, quant_fast<KIND>(x[i], dv, qmin, qmax));
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) f(i, quant_elem<KIND>(x[i], dv, qmin, qmax));
+    }
 }
 
 // c = d y / d s^ (straight-through): q - r inside, the bound outside

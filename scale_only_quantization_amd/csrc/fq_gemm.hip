@@ -175,15 +175,13 @@ __device__ __forceinline__ int xcd_tile(int id, int grid, int tiles) {
     return (id / 8 < chunk && t < tiles) ? t : -1;
 }
 
+// sum of g c over 8 elements sharing the effective scale s
 template <int KIND>
-__device__ __forceinline__ float sg_part4(const float* w4, const float* g4, const Div& dv, float qmin,
-                                          float qmax) {
+__device__ __forceinline__ float sg_part8(const float* w8, const float* g8, float s, float qmin, float qmax) {
     float part = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const Elem el = quant_elem<KIND>(w4[v], dv, qmin, qmax);
-        part = __builtin_fmaf(g4[v], ste_c(el, qmin, qmax), part);
-    }
+    quant_group<KIND, 8>(w8, s, qmin, qmax, [&](int v, const Elem& el) {
+        part = __builtin_fmaf(g8[v], ste_c(el, qmin, qmax), part);
+    });
     return part;
 }
 
@@ -233,24 +231,21 @@ __device__ __forceinline__ void sg_epilogue(const GemmArgs& g, const f32x16 (&ac
 #pragma unroll
         for (int tj = 0; tj < WTN; ++tj) {
             const int jt = j_w + tj * 32;
-            float p[2] = {0.0f, 0.0f};
+            float p[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 // effective scale of the 16-column block (the block's columns
                 // share one scale for every granularity allowed here)
                 float s = sv[cur][tj][b];
                 if (KIND == K_NVFP4) s = t * e4m3_round(fminf(s / t, 448.0f));
-                Div dv;
-                dv.set(s);
+                // this lane's 8 elements of the block: q = 2b, 2b+1, 4 columns each
+                const uint2 wa = wv[cur][tj][2 * b], wb = wv[cur][tj][2 * b + 1];
+                const float w8[8] = {bf_lo(wa.x), bf_hi(wa.x), bf_lo(wa.y), bf_hi(wa.y),
+                                     bf_lo(wb.x), bf_hi(wb.x), bf_lo(wb.y), bf_hi(wb.y)};
+                float g8[8];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int q = 2 * b + h;
-                    const uint2 w = wv[cur][tj][q];
-                    const float w4[4] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
-                    const float g4[4] = {acc[ti][tj][4 * q], acc[ti][tj][4 * q + 1], acc[ti][tj][4 * q + 2],
-                                         acc[ti][tj][4 * q + 3]};
-                    p[b] += sg_part4<KIND>(w4, g4, dv, qmin, qmax);
-                }
+                for (int v = 0; v < 8; ++v) g8[v] = acc[ti][tj][8 * b + v];
+                p[b] = sg_part8<KIND>(w8, g8, s, qmin, qmax);
             }
             const float b0 = p[0] + __shfl_xor(p[0], 32);
             const float b1 = p[1] + __shfl_xor(p[1], 32);
@@ -494,7 +489,13 @@ __global__ __launch_bounds__(64 * WVM * WVN) void k_gemm(GemmArgs g) {
 // (256 / WVM_BIG) x (256 / WVN_BIG); small tile: 128 x 128, 2 x 2 waves.
 constexpr int BK_BIG = GEMM_BK_BIG, S_BIG = GEMM_S_BIG, BK_SMALL = 32, S_SMALL = 3;
 constexpr int WVM_BIG = GEMM_WVM, WVN_BIG = GEMM_WVN;
+#ifdef GEMM_WTM
+constexpr int WTM_BIG = GEMM_WTM, WTN_BIG = GEMM_WTN;
+#else
 constexpr int WTM_BIG = 8 / WVM_BIG, WTN_BIG = 8 / WVN_BIG;
+#endif
+constexpr int BM_BIG = 32 * WTM_BIG * WVM_BIG, BN_BIG = 32 * WTN_BIG * WVN_BIG;
+static_assert(BM_BIG == 256, "the large row tile is the 256-row tile table");
 #define FQ_BIG(MODE) k_gemm<MODE, WVM_BIG, WVN_BIG, WTM_BIG, WTN_BIG, BK_BIG, S_BIG>
 #define FQ_SMALL(MODE) k_gemm<MODE, 2, 2, 2, 2, BK_SMALL, S_SMALL>
 
@@ -510,8 +511,8 @@ template __global__ void FQ_SMALL(WGRAD)(GemmArgs);
 // Large tiles where the shapes allow, 128 x 128 otherwise.
 template <int MODE>
 hipError_t launch(const GemmArgs& g, hipStream_t st) {
-    const bool big_m = MODE == WGRAD ? (g.N % 256 == 0) : true;
-    const bool big_n = (MODE == WGRAD ? g.K : g.N) % 256 == 0;
+    const bool big_m = MODE == WGRAD ? (g.N % BM_BIG == 0) : true;
+    const bool big_n = (MODE == WGRAD ? g.K : g.N) % BN_BIG == 0;
     const int big = (big_m && big_n) ? 1 : 0;
     GemmArgs a = g;
     int64_t blocks;
@@ -520,16 +521,18 @@ hipError_t launch(const GemmArgs& g, hipStream_t st) {
         a.tile_expert = g.tables[big].tile_expert;
         a.tile_row0 = g.tables[big].tile_row0;
         a.num_tiles = g.tables[big].num_tiles;
-        const int bm = big ? 256 : 128;
-        blocks = max_mtiles(g.R, g.E, bm) * (g.N / bm);
+        const int bm = big ? BM_BIG : 128, bn = big ? BN_BIG : 128;
+        blocks = max_mtiles(g.R, g.E, bm) * (g.N / bn);
     } else {
-        // persistent: as many blocks as fit on the device at once (LDS bound:
-        // one large-tile block or two small-tile blocks per CU), 8 groups
-        int dev = 0, cus = 0;
+        // persistent: as many blocks as are resident on the device at once
+        int dev = 0, cus = 0, per_cu = 0;
         hipError_t err = hipGetDevice(&dev);
         if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err == hipSuccess)
+            err = big ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, FQ_BIG(MODE), 64 * WVM_BIG * WVN_BIG, 0)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, FQ_SMALL(MODE), 256, 0);
         if (err != hipSuccess) return err;
-        blocks = (int64_t)(cus > 8 ? cus : 8) * (big ? 1 : 2);
+        blocks = (int64_t)(cus > 8 ? cus : 8) * (per_cu > 1 ? per_cu : 1);
     }
     blocks = (blocks + 7) / 8 * 8;       // a whole number of blocks per XCD
     if (big) hipLaunchKernelGGL((FQ_BIG(MODE)), dim3((unsigned)blocks), dim3(64 * WVM_BIG * WVN_BIG), 0, st, a);

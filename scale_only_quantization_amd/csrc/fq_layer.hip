@@ -200,25 +200,18 @@ __device__ __forceinline__ float act_scale(const ActQ& a, int e, float bm, float
 
 template <int KIND>
 __device__ __forceinline__ void quant8(const float* f, float s, float qmin, float qmax, float* y) {
-    Div dv;
-    dv.set(s);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = quant_elem<KIND>(f[i], dv, qmin, qmax).q * s;
+    quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) { y[i] = e.q * s; });
 }
 
 // straight-through terms of 8 elements: sum g*c, and the pass mask applied to g
 template <int KIND>
 __device__ __forceinline__ float ste8(const float* f, const float* g, float s, float qmin, float qmax,
                                       bool dyn, float* gx) {
-    Div dv;
-    dv.set(s);
     float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const Elem el = quant_elem<KIND>(f[i], dv, qmin, qmax);
+    quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& el) {
         part = __builtin_fmaf(g[i], ste_c(el, qmin, qmax), part);
         gx[i] = dyn ? g[i] : g[i] * (el.inside ? 1.0f : 0.0f);   // g * mask (signed zero)
-    }
+    });
     return part;
 }
 

@@ -96,19 +96,15 @@ __global__ __launch_bounds__(TPB) void k_tensor_fwd(TensorArgs a) {
             float dfac;
             uint32_t bc;
             const float s = vec_scale<KIND, DYN>(a, grow, b, v, f, row_s, t, &dfac, &bc);
-            Div dv;
-            dv.set(s);
             float yv[8];
             uint32_t c4 = 0;
             uint32_t c8[2] = {0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                Elem e = quant_elem<KIND>(f[i], dv, qmin, qmax);
+            quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) {
                 yv[i] = e.q * s;
-                uint32_t c = elem_code<KIND>(e, f[i]);
+                const uint32_t c = elem_code<KIND>(e, f[i]);
                 c4 |= (c & 0xFu) << (4 * i);
                 c8[i >> 2] |= (c & 0xFFu) << (8 * (i & 3));
-            }
+            });
             if (a.y) reinterpret_cast<uint4*>(a.y + grow * a.cols)[v] = pack8(yv);
             if (a.codes) {
                 if (four_bit)
@@ -162,17 +158,13 @@ __global__ __launch_bounds__(TPB) void k_tensor_bwd(TensorArgs a) {
             float dfac;
             uint32_t bc;
             const float s = vec_scale<KIND, DYN>(a, grow, b, v, f, row_s, t, &dfac, &bc);
-            Div dv;
-            dv.set(s);
             float gx[8];
             float part = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                Elem e = quant_elem<KIND>(f[i], dv, qmin, qmax);
+            quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) {
                 const float c = ste_c(e, qmin, qmax);
                 gx[i] = DYN ? g[i] : g[i] * (e.inside ? 1.0f : 0.0f);   // g * mask (signed zero)
                 part = __builtin_fmaf(g[i], c, part);
-            }
+            });
             if (a.gx) reinterpret_cast<uint4*>(a.gx + grow * a.cols)[v] = pack8(gx);
             if (a.gscale) {
                 if (KIND == K_NVFP4) {
