@@ -88,7 +88,7 @@ struct Section {
 
 struct Layout {
     // saved
-    Section counts, offsets, row_of, src_of, tile_expert[2], tile_row0[2], num_tiles, order, wg_list, wg_cnt;
+    Section counts, offsets, row_of, src_of, row_expert, tile_expert[2], tile_row0[2], num_tiles, order, wg_list, wg_cnt;
     Section w1hat, w2hat, xhat, z1, hhat, yr;
     size_t saved = 0;
     // workspace
@@ -143,6 +143,7 @@ Layout layout(const fq_layer_desc* L, const LayerQ& q) {
     place(y.offsets, (E + 1) * 4, c);
     place(y.row_of, R * 4, c);
     place(y.src_of, R * 4, c);
+    place(y.row_expert, R * 4, c);
     for (int h = 0; h < 2; ++h) {
         const int64_t mt = max_mtiles(R, (int)E, TILE_HEIGHTS[h]);
         place(y.tile_expert[h], mt * 4, c);
@@ -393,6 +394,7 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     ra.offsets = at<int32_t>(saved, lay.offsets);
     ra.row_of = at<int32_t>(saved, lay.row_of);
     ra.src_of = at<int32_t>(saved, lay.src_of);
+    ra.row_expert = at<int32_t>(saved, lay.row_expert);
     for (int h = 0; h < 2; ++h) {
         ra.tables[h].tile_expert = at<int32_t>(saved, lay.tile_expert[h]);
         ra.tables[h].tile_row0 = at<int32_t>(saved, lay.tile_row0[h]);
@@ -475,8 +477,7 @@ int fq_grouped_expert_fwd(const fq_layer_desc* L, const fq_expert_params* P, con
     // F5: SwiGLU + A2
     SwigluArgs sa{};
     sa.z1 = at<uint16_t>(saved, lay.z1);
-    sa.ids = topk_ids;
-    sa.src_of = ra.src_of;
+    sa.row_expert = ra.row_expert;
     sa.hhat = at<uint16_t>(saved, lay.hhat);
     sa.R = R;
     sa.I = I;
@@ -635,8 +636,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
     SwigluBwdArgs sb{};
     sb.z1 = at<uint16_t>(saved, lay.z1);
     sb.dhh = dhh;
-    sb.ids = topk_ids;
-    sb.src_of = src_of;
+    sb.row_expert = at<int32_t>(saved, lay.row_expert);
     sb.dz1 = dz1;
     sb.rowpart = G->ds_a2 ? at<float>(workspace, lay.rowpart2) : nullptr;
     sb.R = R;

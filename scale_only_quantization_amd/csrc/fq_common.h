@@ -87,10 +87,13 @@ __device__ __forceinline__ float e4m3_round(float a) {
 // E2M1 round-to-nearest-even of a magnitude in [0, 6]: spacing 0.5 below 2,
 // 1 in [2, 4), 2 in [4, 6]; rint breaks ties to the even multiple, which is
 // the even code.
+// Computed as (a + C) - C with C = 2^22, 2^23, 2^24 for spacing 0.5, 1, 2:
+// the fp32 sum rounds a to a multiple of ulp(C), ties to the even multiple;
+// C = 2^(21 + clamp(exponent of a, 1, 3)) with a = m 2^e, m in [0.5, 1).
 __device__ __forceinline__ float e2m1_round(float a) {
-    float sp = a >= 4.0f ? 2.0f : (a >= 2.0f ? 1.0f : 0.5f);
-    float inv = a >= 4.0f ? 0.5f : (a >= 2.0f ? 1.0f : 2.0f);
-    return rintf(a * inv) * sp;
+    const int e = __builtin_amdgcn_frexp_expf(a);
+    const float c = __uint_as_float((uint32_t)(min(max(e, 1), 3) + 148) << 23);   // 2^(21 + e)
+    return (a + c) - c;
 }
 // 3-bit magnitude code of an E2M1 grid value
 __device__ __forceinline__ uint32_t e2m1_code(float qm) {

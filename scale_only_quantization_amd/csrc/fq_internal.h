@@ -52,6 +52,7 @@ struct RouteArgs {
     int32_t* offsets;      // [E+1]
     int32_t* row_of;       // [R]
     int32_t* src_of;       // [R]
+    int32_t* row_expert;   // [R] expert of each routed row
     TileTable tables[2];   // heights 128 and 256
     int32_t* order;        // [E] experts by descending count
     int32_t* wg_list;      // [8, E] experts of each XCD's weight-gradient work, descending
@@ -82,8 +83,7 @@ hipError_t launch_permute_a1(const PermuteArgs& a, hipStream_t st);
 
 struct SwigluArgs {        // z1 [R, 2I] -> hhat [R, I] (fq_a2 per expert)
     const uint16_t* z1;
-    const int32_t* ids;
-    const int32_t* src_of;
+    const int32_t* row_expert;
     uint16_t* hhat;
     int64_t R;
     int I, E;
@@ -116,8 +116,7 @@ hipError_t launch_permute_dy(const PermuteDyArgs& a, hipStream_t st);
 struct SwigluBwdArgs {     // (z1, dhhat) -> dz1, per-row partial of ds_a2
     const uint16_t* z1;
     const uint16_t* dhh;
-    const int32_t* ids;
-    const int32_t* src_of;
+    const int32_t* row_expert;
     uint16_t* dz1;
     float* rowpart;        // [R] or null
     int64_t R;

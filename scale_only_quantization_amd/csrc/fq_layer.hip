@@ -24,6 +24,29 @@ __device__ __forceinline__ int clamp_id(int id, int E) { return id < 0 ? 0 : (id
 // routed-row indices read back from the routing tables, kept in [0, R)
 __device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t R) { return r < 0 ? 0 : (r >= R ? R - 1 : r); }
 
+// The k routing slots of token t in one load: lane j < k holds slot j's
+// expert, routed row and weight; slot j is then read with a wave-uniform
+// readlane (k <= 64).
+struct Slots {
+    int e, row;
+    float w;
+};
+__device__ __forceinline__ Slots load_slots(const int32_t* ids, const int32_t* row_of, const float* w, int64_t t,
+                                            int k, int E, int64_t R, int lane) {
+    Slots s{0, 0, 0.0f};
+    if (lane < k) {
+        const int64_t fi = t * k + lane;
+        if (ids) s.e = clamp_id(ids[fi], E);
+        s.row = (int)clamp_row(row_of[fi], R);
+        if (w) s.w = w[fi];
+    }
+    return s;
+}
+__device__ __forceinline__ int slot_i(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+__device__ __forceinline__ float slot_f(float v, int j) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+
 // ------------------------------------------------------------------ routing --
 // Per block of RB flat indices: histogram and the stable rank of each element
 // among equal ids inside the block.  Equal ids inside a 64-element wave slice
@@ -167,7 +190,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
 
 __global__ __launch_bounds__(TPB) void k_route_scatter(const int32_t* ids, int64_t R, int E,
                                                        const int32_t* hist, const int32_t* local_rank,
-                                                       int32_t* row_of, int32_t* src_of) {
+                                                       int32_t* row_of, int32_t* src_of, int32_t* row_expert) {
     const int64_t i0 = (int64_t)blockIdx.x * RB;
     for (int j = threadIdx.x; j < RB; j += TPB) {
         const int64_t i = i0 + j;
@@ -175,7 +198,10 @@ __global__ __launch_bounds__(TPB) void k_route_scatter(const int32_t* ids, int64
         const int id = clamp_id(ids[i], E);
         const int row = hist[(int64_t)blockIdx.x * E + id] + local_rank[i];
         row_of[i] = row;
-        if (row >= 0 && row < R) src_of[row] = (int32_t)i;
+        if (row >= 0 && row < R) {
+            src_of[row] = (int32_t)i;
+            row_expert[row] = id;
+        }
     }
 }
 
@@ -262,10 +288,10 @@ __global__ __launch_bounds__(TPB) void k_permute_a1(PermuteArgs a) {
                 qv[c] = pack8(y);
             }
         }
+        const Slots sl = load_slots(a.ids, a.row_of, nullptr, t, a.k, a.E, a.T * a.k, lane);
         for (int j = 0; j < a.k; ++j) {
-            const int64_t fi = t * a.k + j;
-            const int e = clamp_id(a.ids[fi], a.E);
-            const int64_t row = clamp_row(a.row_of[fi], a.T * a.k);
+            const int e = slot_i(sl.e, j);
+            const int64_t row = slot_i(sl.row, j);
             uint4* dst = reinterpret_cast<uint4*>(a.xhat + row * a.H);
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
@@ -317,7 +343,7 @@ __global__ __launch_bounds__(TPB) void k_swiglu_a2(SwigluArgs a) {
     const float qmin = a.a2.q.qmin, qmax = a.a2.q.qmax;
     const int gl = a.a2.q.group >> 3;
     for (int64_t r = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); r < a.R; r += (int64_t)gridDim.x * RPB) {
-        const int e = clamp_id(a.ids[clamp_row(a.src_of[r], a.R)], a.E);
+        const int e = clamp_id(a.row_expert[r], a.E);
         const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + r * 2 * (int64_t)a.I);
         uint4 hv[NV];
         float bm[NV];
@@ -371,23 +397,33 @@ __global__ __launch_bounds__(TPB) void k_combine(CombineArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int nvec = a.H >> 3;
     for (int64_t t = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); t < a.T; t += (int64_t)gridDim.x * RPB) {
+        const Slots sl = load_slots(nullptr, a.row_of, a.w, t, a.k, 1, a.T * a.k, lane);
         float acc[NV][8];
 #pragma unroll
         for (int c = 0; c < NV; ++c)
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
-        for (int j = 0; j < a.k; ++j) {
-            const int64_t fi = t * a.k + j;
-            const float w = a.w[fi];
-            const uint4* src = reinterpret_cast<const uint4*>(a.yr + clamp_row(a.row_of[fi], a.T * a.k) * a.H);
+        // row j+1 is loaded while row j is accumulated
+        uint4 cur[NV], nxt[NV] = {};
+        auto load = [&](int j, uint4* dst) {
+            const uint4* src = reinterpret_cast<const uint4*>(a.yr + (int64_t)slot_i(sl.row, j) * a.H);
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
                 const int v = lane + c * WAVE;
-                if (v >= nvec) continue;
+                dst[c] = v < nvec ? src[v] : make_uint4(0, 0, 0, 0);
+            }
+        };
+        load(0, cur);
+        for (int j = 0; j < a.k; ++j) {
+            if (j + 1 < a.k) load(j + 1, nxt);
+            const float w = slot_f(sl.w, j);
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
                 float f[8];
-                unpack8(src[v], f);
+                unpack8(cur[c], f);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[c][i] = acc[c][i] + w * f[i];
+                cur[c] = nxt[c];
             }
         }
 #pragma unroll
@@ -404,6 +440,7 @@ __global__ __launch_bounds__(TPB) void k_permute_dy(PermuteDyArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int nvec = a.H >> 3;
     for (int64_t t = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); t < a.T; t += (int64_t)gridDim.x * RPB) {
+        const Slots sl = load_slots(nullptr, a.row_of, a.w, t, a.k, 1, a.T * a.k, lane);
         float d[NV][8];
 #pragma unroll
         for (int c = 0; c < NV; ++c) {
@@ -413,29 +450,40 @@ __global__ __launch_bounds__(TPB) void k_permute_dy(PermuteDyArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) d[c][i] = 0.0f;
         }
+        // with d topk_w: Y_r row j+1 is loaded while row j is reduced
+        uint4 cur[NV], nxt[NV] = {};
+        auto load = [&](int j, uint4* dst) {
+            const uint4* src = reinterpret_cast<const uint4*>(a.yr + (int64_t)slot_i(sl.row, j) * a.H);
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                const int v = lane + c * WAVE;
+                dst[c] = v < nvec ? src[v] : make_uint4(0, 0, 0, 0);
+            }
+        };
+        if (a.dw) load(0, cur);
         for (int j = 0; j < a.k; ++j) {
-            const int64_t fi = t * a.k + j;
-            const float w = a.w[fi];
-            const int64_t row = clamp_row(a.row_of[fi], a.T * a.k);
+            if (a.dw && j + 1 < a.k) load(j + 1, nxt);
+            const float w = slot_f(sl.w, j);
+            const int64_t row = slot_i(sl.row, j);
             float part = 0.0f;
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
                 const int v = lane + c * WAVE;
-                if (v >= nvec) continue;
                 float o[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) o[i] = w * d[c][i];
-                reinterpret_cast<uint4*>(a.dyr + row * a.H)[v] = pack8(o);
+                if (v < nvec) reinterpret_cast<uint4*>(a.dyr + row * a.H)[v] = pack8(o);
                 if (a.dw) {
                     float yv[8];
-                    unpack8(reinterpret_cast<const uint4*>(a.yr + row * a.H)[v], yv);
+                    unpack8(cur[c], yv);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) part = __builtin_fmaf(d[c][i], yv[i], part);
+                    cur[c] = nxt[c];
                 }
             }
             if (a.dw) {
                 part = wave_sum(part);
-                if (lane == 0) a.dw[fi] = part;
+                if (lane == 0) a.dw[t * a.k + j] = part;
             }
         }
     }
@@ -453,7 +501,7 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
     // the gradient straight and own no parameter.
     const bool recompute = KIND == K_NVFP4 || (KIND != K_NONE && !dyn);
     for (int64_t r = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); r < a.R; r += (int64_t)gridDim.x * RPB) {
-        const int e = clamp_id(a.ids[clamp_row(a.src_of[r], a.R)], a.E);
+        const int e = clamp_id(a.row_expert[r], a.E);
         const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + r * 2 * (int64_t)a.I);
         const uint4* dr = reinterpret_cast<const uint4*>(a.dhh + r * a.I);
         uint4* out = reinterpret_cast<uint4*>(a.dz1 + r * 2 * (int64_t)a.I);
@@ -539,10 +587,10 @@ __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
         for (int c = 0; c < NV; ++c)
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
+        const Slots sl = load_slots(a.ids, a.row_of, nullptr, t, a.k, a.E, a.T * a.k, lane);
         for (int j = 0; j < a.k; ++j) {
-            const int64_t fi = t * a.k + j;
-            const int e = clamp_id(a.ids[fi], a.E);
-            const int64_t row = clamp_row(a.row_of[fi], a.T * a.k);
+            const int e = slot_i(sl.e, j);
+            const int64_t row = slot_i(sl.row, j);
             const uint4* src = reinterpret_cast<const uint4*>(a.dxh + row * a.H);
             float part_row = 0.0f;
 #pragma unroll
@@ -625,7 +673,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nblk == 0) return err;
     hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nblk), dim3(TPB), 0, st, a.ids, a.R, a.E, a.hist,
-                       a.local_rank, a.row_of, a.src_of);
+                       a.local_rank, a.row_of, a.src_of, a.row_expert);
     return hipGetLastError();
 }
 
