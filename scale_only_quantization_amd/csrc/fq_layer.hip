@@ -112,12 +112,16 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
     __shared__ int32_t s_c[1024];
     const int e = threadIdx.x;
     int running = 0;
-    if (e < E) {
-        for (int b = 0; b < nblk; ++b) {
-            const int h = hist[(int64_t)b * E + e];
-            hist[(int64_t)b * E + e] = running;
-            running += h;
+    if (e < E) {                       // the column's total, 8 independent loads at a time
+        int b = 0;
+        for (; b + 8 <= nblk; b += 8) {
+            int h[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) h[u] = hist[(int64_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) running += h[u];
         }
+        for (; b < nblk; ++b) running += hist[(int64_t)b * E + e];
     }
     const int cnt = e < E ? running : 0;
     const int m1 = (cnt + 127) / 128, m2 = (cnt + 255) / 256;
@@ -162,7 +166,23 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
         }
         order[rank] = e;
         s_ord[rank] = e;
-        for (int b = 0; b < nblk; ++b) hist[(int64_t)b * E + e] += off;
+        // each block's first row of expert e: off + the exclusive prefix over blocks
+        int acc = off, b = 0;
+        for (; b + 8 <= nblk; b += 8) {
+            int h[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) h[u] = hist[(int64_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                hist[(int64_t)(b + u) * E + e] = acc;
+                acc += h[u];
+            }
+        }
+        for (; b < nblk; ++b) {
+            const int h = hist[(int64_t)b * E + e];
+            hist[(int64_t)b * E + e] = acc;
+            acc += h;
+        }
     }
     __syncthreads();
     // Weight-gradient work per XCD (each XCD has its own L2): experts in
