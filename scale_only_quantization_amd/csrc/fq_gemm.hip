@@ -276,7 +276,7 @@ __device__ __forceinline__ void sg_epilogue(const GemmArgs& g, const f32x16 (&ac
 }
 
 template <int MODE, int WVM, int WVN, int WTM, int WTN, int BK, int S>
-__global__ __launch_bounds__(64 * WVM * WVN) void k_gemm(GemmArgs g) {
+__global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmArgs g) {
     constexpr int NW = WVM * WVN;
     constexpr int BM = 32 * WTM * WVM, BN = 32 * WTN * WVN;
     typedef typename std::conditional<MODE == WGRAD, MNTile<BM, BK, NW>, KTile<BM, BK, NW>>::type ATile;
@@ -284,7 +284,9 @@ __global__ __launch_bounds__(64 * WVM * WVN) void k_gemm(GemmArgs g) {
     constexpr int A_BYTES = ATile::BYTES, STAGE = ATile::BYTES + BTile::BYTES;
     constexpr int LOADS = ATile::PER_WAVE + BTile::PER_WAVE;     // wave load instructions per stage
     static_assert(S >= 2 && S <= 4, "stages");
-    __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE];
+    // the stages; FWD/DGRAD reuse them for the bf16 output tile
+    constexpr int SMEM = (MODE != WGRAD && BM * BN * 2 > S * STAGE) ? BM * BN * 2 : S * STAGE;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
     lds_t* smem = (lds_t*)smem_raw;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) void k_gemm(GemmArgs g) {
         // 16-B chunks are XOR-swizzled by (row & 15), then each wave copies
         // two rows per instruction (16 B per lane) to C.
         constexpr int RB = BN * 2, CH = BN / 8;                 // row bytes, 16-B chunks per row
-        static_assert(BM * RB <= S * STAGE, "C tile fits the LDS stages");
+        static_assert(BM * RB <= SMEM, "C tile fits the LDS");
         __syncthreads();                                         // every wave is done with the stages
 #pragma unroll
         for (int ti = 0; ti < WTM; ++ti) {
