@@ -118,15 +118,15 @@ __global__ __launch_bounds__(TPB) void k_tensor_fwd(TensorArgs a) {
     }
 }
 
-__device__ __forceinline__ void load_grad8(const TensorArgs& a, int64_t grow, int v, float* g) {
+__device__ __forceinline__ void load_grad8(const TensorArgs& a, int64_t grow, int v, float* g, int64_t gv = -1) {
+    if (gv < 0) gv = grow * (a.cols >> 3) + v;             // flat vector index
     if (a.gy_fp32) {
-        const float4* p = reinterpret_cast<const float4*>(
-            static_cast<const float*>(a.gy) + grow * a.cols) + 2 * v;
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.gy)) + 2 * gv;
         float4 u0 = p[0], u1 = p[1];
         g[0] = u0.x; g[1] = u0.y; g[2] = u0.z; g[3] = u0.w;
         g[4] = u1.x; g[5] = u1.y; g[6] = u1.z; g[7] = u1.w;
     } else {
-        unpack8(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.gy) + grow * a.cols)[v], g);
+        unpack8(reinterpret_cast<const uint4*>(a.gy)[gv], g);
     }
 }
 
@@ -193,6 +193,104 @@ __global__ __launch_bounds__(TPB) void k_tensor_bwd(TensorArgs a) {
     }
 }
 
+// Flat layout: one lane per 8-element vector of a matrix (blockIdx.y is the
+// batch index), so that a wave reads and writes 1 KB contiguous whatever the
+// row length (rows of 768 leave a row-per-wave kernel a quarter idle).  Used
+// for NVFP4 block scales and per-group scales, whose index is the vector's
+// flat index over 2 or group/8: blocks and groups align with lane pairs and
+// lane groups because the row length is a multiple of the block or group.
+template <int KIND, bool DYN>
+__device__ __forceinline__ float flat_scale(const TensorArgs& a, int64_t gv, int sh, const float* f, float t,
+                                            uint32_t* bc) {
+    if (KIND == K_NVFP4) {
+        float ratio;
+        if (DYN) {
+            float m = amax8(f);
+            m = fmaxf(m, __shfl_xor(m, 1));                 // 16-element block = lane pair
+            ratio = m / (6.0f * t);
+        } else {
+            ratio = a.scale[gv >> 1] / t;
+        }
+        return t * e4m3_round(fminf(ratio, 448.0f), bc);
+    }
+    *bc = 0;
+    if (DYN) return group_max(amax8(f), a.q.group >> 3) / a.q.qdiv;
+    return a.scale[gv >> sh];
+}
+
+template <int KIND, bool DYN>
+__global__ __launch_bounds__(TPB) void k_tensor_fwd_flat(TensorArgs a) {
+    const int64_t per = a.rows * (a.cols >> 3);             // vectors per matrix
+    const int64_t b = blockIdx.y;
+    const int sh = __builtin_ctz((unsigned)(a.q.group >> 3));   // group vectors = 2^sh
+    const float qmin = a.q.qmin, qmax = a.q.qmax;
+    const bool four_bit = (KIND == K_NVFP4) || (KIND == K_INT && qmax - qmin < 16.0f);
+    const float t = (KIND == K_NVFP4) ? a.tscale[b] : 0.0f;
+    for (int64_t gm = (int64_t)blockIdx.x * TPB + threadIdx.x; gm < per; gm += (int64_t)gridDim.x * TPB) {
+        const int64_t gv = b * per + gm;
+        float f[8];
+        unpack8(reinterpret_cast<const uint4*>(a.x)[gv], f);
+        uint32_t bc;
+        const float s = flat_scale<KIND, DYN>(a, gv, sh, f, t, &bc);
+        float yv[8];
+        uint32_t c4 = 0;
+        uint32_t c8[2] = {0u, 0u};
+        quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) {
+            yv[i] = e.q * s;
+            const uint32_t c = elem_code<KIND>(e, f[i]);
+            c4 |= (c & 0xFu) << (4 * i);
+            c8[i >> 2] |= (c & 0xFFu) << (8 * (i & 3));
+        });
+        if (a.y) reinterpret_cast<uint4*>(a.y)[gv] = pack8(yv);
+        if (a.codes) {
+            if (four_bit) reinterpret_cast<uint32_t*>(a.codes)[gv] = c4;
+            else reinterpret_cast<uint2*>(a.codes)[gv] = make_uint2(c8[0], c8[1]);
+        }
+        if (KIND == K_NVFP4 && a.bcodes && !(gv & 1)) a.bcodes[gv >> 1] = (uint8_t)bc;
+    }
+}
+
+template <int KIND, bool DYN>
+__global__ __launch_bounds__(TPB) void k_tensor_bwd_flat(TensorArgs a) {
+    const int64_t nvec_row = a.cols >> 3;
+    const int64_t per = a.rows * nvec_row;
+    const int64_t b = blockIdx.y;
+    const int sh = __builtin_ctz((unsigned)(a.q.group >> 3));
+    const float qmin = a.q.qmin, qmax = a.q.qmax;
+    constexpr bool PASS_ONLY = DYN && KIND != K_NVFP4;
+    const float t = (KIND == K_NVFP4) ? a.tscale[b] : 0.0f;
+    for (int64_t gm = (int64_t)blockIdx.x * TPB + threadIdx.x; gm < per; gm += (int64_t)gridDim.x * TPB) {
+        const int64_t gv = b * per + gm;
+        float g[8];
+        load_grad8(a, 0, (int)0, g, gv);
+        if (PASS_ONLY) {
+            if (a.gx) reinterpret_cast<uint4*>(a.gx)[gv] = pack8(g);
+            continue;
+        }
+        float f[8];
+        unpack8(reinterpret_cast<const uint4*>(a.x)[gv], f);
+        uint32_t bc;
+        const float s = flat_scale<KIND, DYN>(a, gv, sh, f, t, &bc);
+        float gx[8];
+        float part = 0.0f;
+        quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) {
+            const float c = ste_c(e, qmin, qmax);
+            gx[i] = g[i] * (e.inside ? 1.0f : 0.0f);   // g * mask (signed zero)
+            part = __builtin_fmaf(g[i], c, part);
+        });
+        if (a.gx) reinterpret_cast<uint4*>(a.gx)[gv] = pack8(gx);
+        if (a.gscale) {
+            if (KIND == K_NVFP4) {
+                const float tot = part + __shfl_xor(part, 1);
+                if (!(gv & 1)) a.gscale[gv >> 1] = tot;
+            } else {
+                const float tot = group_sum(part, 1 << sh);
+                if ((gv & ((1 << sh) - 1)) == 0) a.gscale[gv >> sh] = tot;
+            }
+        }
+    }
+}
+
 // grad of a per-matrix parameter: sum of the rows' partials, fixed order
 __global__ __launch_bounds__(TPB) void k_rows_to_batch(const float* rowpart, int64_t rows, float* out) {
     __shared__ float red[TPB];
@@ -223,6 +321,11 @@ __global__ __launch_bounds__(TPB) void k_copy_bf16(const uint16_t* src, int src_
     }
 }
 
+int64_t grid_flat(int64_t nvec) {
+    int64_t g = (nvec + TPB - 1) / TPB;
+    return g < 1 ? 1 : (g > (1 << 22) ? (1 << 22) : g);
+}
+
 int64_t grid_rows(int64_t nrows) {
     int64_t g = (nrows + RPB - 1) / RPB;
     return g < 1 ? 1 : (g > (1 << 22) ? (1 << 22) : g);
@@ -243,6 +346,15 @@ size_t tensor_workspace_bytes(const QParams& q, int64_t batch, int64_t rows) {
 #define FQ_LAUNCH(KERNEL, KIND, DYN)                                                       \
     hipLaunchKernelGGL((KERNEL<KIND, DYN>), dim3((unsigned)grid_rows(a.batch * a.rows)),   \
                        dim3(TPB), 0, st, a)
+#define FQ_LAUNCH_FLAT(KERNEL, KIND, DYN)                                                  \
+    hipLaunchKernelGGL((KERNEL<KIND, DYN>), dim3((unsigned)grid_flat(a.rows * (a.cols >> 3)), (unsigned)a.batch), \
+                       dim3(TPB), 0, st, a)
+#define FQ_KINDS(KERNEL, LAUNCH)                                                            \
+    switch (a.q.kind) {                                                                     \
+    case K_NVFP4: if (dyn) LAUNCH(KERNEL, K_NVFP4, true); else LAUNCH(KERNEL, K_NVFP4, false); break; \
+    case K_INT: if (dyn) LAUNCH(KERNEL, K_INT, true); else LAUNCH(KERNEL, K_INT, false); break;       \
+    default: if (dyn) LAUNCH(KERNEL, K_FP8, true); else LAUNCH(KERNEL, K_FP8, false); break;          \
+    }
 
 hipError_t launch_tensor_fwd(const TensorArgs& a, hipStream_t st) {
     const int64_t nrows = a.batch * a.rows;
@@ -256,9 +368,13 @@ hipError_t launch_tensor_fwd(const TensorArgs& a, hipStream_t st) {
                            a.x, 0, nullptr, a.y, nvec);
         break;
     }
-    case K_NVFP4: if (dyn) FQ_LAUNCH(k_tensor_fwd, K_NVFP4, true); else FQ_LAUNCH(k_tensor_fwd, K_NVFP4, false); break;
-    case K_INT: if (dyn) FQ_LAUNCH(k_tensor_fwd, K_INT, true); else FQ_LAUNCH(k_tensor_fwd, K_INT, false); break;
-    case K_FP8: if (dyn) FQ_LAUNCH(k_tensor_fwd, K_FP8, true); else FQ_LAUNCH(k_tensor_fwd, K_FP8, false); break;
+    case K_NVFP4:
+    case K_INT:
+    case K_FP8:
+        // NVFP4 blocks and groups flat; per-row / per-tensor scales a row per wave
+        if ((a.q.kind == K_NVFP4 || a.q.gran == G_GROUP) && a.batch <= 65535) { FQ_KINDS(k_tensor_fwd_flat, FQ_LAUNCH_FLAT) }
+        else { FQ_KINDS(k_tensor_fwd, FQ_LAUNCH) }
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -276,9 +392,16 @@ hipError_t launch_tensor_bwd(const TensorArgs& a, hipStream_t st) {
                            static_cast<const uint16_t*>(a.gy), a.gy_fp32, a.gy, a.gx, nvec);
         return hipGetLastError();
     }
-    case K_NVFP4: if (dyn) FQ_LAUNCH(k_tensor_bwd, K_NVFP4, true); else FQ_LAUNCH(k_tensor_bwd, K_NVFP4, false); break;
-    case K_INT: if (dyn) FQ_LAUNCH(k_tensor_bwd, K_INT, true); else FQ_LAUNCH(k_tensor_bwd, K_INT, false); break;
-    case K_FP8: if (dyn) FQ_LAUNCH(k_tensor_bwd, K_FP8, true); else FQ_LAUNCH(k_tensor_bwd, K_FP8, false); break;
+    case K_NVFP4:
+    case K_INT:
+    case K_FP8: {
+        // row reductions (per-row / per-tensor gradients, the NVFP4 tensor
+        // scale of dynamic blocks) need a row per wave; else flat
+        const bool flat = (a.q.kind == K_NVFP4 ? !dyn : (dyn || a.q.gran == G_GROUP)) && a.batch <= 65535;
+        if (flat) { FQ_KINDS(k_tensor_bwd_flat, FQ_LAUNCH_FLAT) }
+        else { FQ_KINDS(k_tensor_bwd, FQ_LAUNCH) }
+        break;
+    }
     default: return hipErrorInvalidValue;
     }
     hipError_t err = hipGetLastError();
