@@ -98,6 +98,12 @@ class HipEvents:
             out.append(h.value)
         return out
 
+    def record(self, e, stream=None):
+        assert self.rt.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) == 0
+
+    def sync(self, e):
+        assert self.rt.hipEventSynchronize(ctypes.c_void_p(e)) == 0
+
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
         assert self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
@@ -150,6 +156,54 @@ def sources_sha(kernel):
     for n in sorted(KERNELS[kernel][1] + COMMON_SOURCES):
         h.update(open(os.path.join(d, n), "rb").read())
     return h.hexdigest()[:16]
+
+
+def fake_quant_stack(ev, F, reps=20, warmup=3):
+    """Standalone fq_tensor on the weight-only microbench stack: 128 expert
+    matrices 768 x 2048 bf16 N(0, 0.02) with 0.1% outliers x 20, NVFP4 block-16
+    and INT4 group-128 with learnable fp32 scales; forward (y), then the
+    straight-through scale gradient from an fp32 upstream gradient.  Per call:
+    average over `reps` back-to-back calls between two events."""
+    import torch
+
+    import synth
+    from oracle import presets as OP
+    from tests.fq_testutil import qdesc_of, to_dev_bf16
+    W, G = synth.make_weight_stack()
+    E, N, K = W.shape
+    n = W.size
+    x = to_dev_bf16(W)
+    g = torch.from_numpy(G).cuda()
+    del G
+    y = torch.empty_like(x)
+    out = {}
+    for name, q, kind in (("nvfp4", OP.NVFP4_W, "nvfp4"), ("int4_g128", OP.INT4_G128, "int4_g")):
+        c = synth.calibrate_weight(kind, W, group=128)
+        s = torch.from_numpy(c["s"]).cuda()
+        t = torch.from_numpy(c["t"]).cuda() if "t" in c else None
+        ds = torch.empty_like(s)
+        qd = qdesc_of(q)
+        nscale = s.numel() * 4
+        e0, e1 = ev.create(2)
+        res = {}
+        for pass_, fn, alg in (
+                ("fwd", lambda: F.fq_tensor(qd, x, s, t, y=y), 4 * n + nscale),
+                ("bwd", lambda: F.fq_tensor(qd, x, s, t, grad_y=g, grad_scale=ds), 6 * n + 2 * nscale)):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            ev.record(e0)
+            for _ in range(reps):
+                fn()
+            ev.record(e1)
+            ev.sync(e1)
+            ms = ev.elapsed_ms(e0, e1) / reps
+            gbs = alg / (ms * 1e-3) / 1e9
+            res[pass_] = dict(ms=round(ms, 4), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 3),
+                              bytes=alg)
+        out[name] = res
+    out["shape"] = [E, N, K]
+    return out
 
 
 def cpu_baseline(data, P, fmt, quantiles=tuple(np.linspace(0.02, 0.98, 25))):
@@ -307,6 +361,12 @@ def main():
         "roofline": roof,
         "stages": stages,
     }
+    del dl
+    torch.cuda.empty_cache()
+    print("[bench] weight-only fake-quant microbench ...", file=sys.stderr, flush=True)
+    out["fake_quant"] = fake_quant_stack(ev, F)
+    if args.stages:
+        print(f"[bench] fake_quant {out['fake_quant']}", file=sys.stderr)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a bounded sample ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(data, P, fmt)
