@@ -31,6 +31,9 @@ CASES = [
     ("fp8_tensor", OP.FP8_TENSOR, (2, 9, 512)),
     ("int4_dyn_g32", QSpec("int", "group", 32, "dynamic", -8, 7), (2, 10, 320)),
     ("int8_g64_static", QSpec("int", "group", 64, "static", -128, 127), (1, 12, 256)),
+    # more matrices than one launch grid dimension holds (65535): the row-per-wave path
+    ("nvfp4_w_many", OP.NVFP4_W, (70000, 1, 32)),
+    ("int4_g128_many", OP.INT4_G128, (66000, 1, 128)),
 ]
 
 

@@ -213,6 +213,13 @@ def test_layer_ragged_tiles_and_wide_hidden():
     _full_parity(L, data, P, Po)
 
 
+@pytest.mark.parametrize("H,I", [(8192, 256), (256, 8192)], ids=["hidden8192", "intermediate8192"])
+def test_layer_largest_hidden_and_intermediate(H, I):
+    # the largest widths the library accepts (16 vectors of 8 per lane per row)
+    L, data, P, Po = _case("nvfp4", 2, H, I, 40, 2, seed=17)
+    _full_parity(L, data, P, Po, end_to_end=False)
+
+
 def test_layer_empty_expert_and_single_expert():
     L, data, P, Po = _case("nvfp4", 8, 256, 128, 200, 1, seed=5)
     data["ids"][:] = 3                           # every token to expert 3; the others empty
