@@ -162,7 +162,8 @@ __device__ __forceinline__ Elem quant_fast(float x, const Div& d, float qmin, fl
     const float r = __builtin_fmaf(rem, d.inv, q0);
     Elem e;
     e.r = r;
-    e.inside = (r >= qmin) && (r <= qmax);
+    // NVFP4 and FP8 grids are symmetric (qmin = -qmax)
+    e.inside = KIND == K_INT ? (r >= qmin) && (r <= qmax) : fabsf(r) <= qmax;
     e.q = grid_q<KIND>(r, x, qmin, qmax);
     return e;
 }
@@ -183,9 +184,14 @@ __device__ __forceinline__ void quant_group(const float* x, float s, float qmin,
     }
 }
 
-// c = d y / d s^ (straight-through): q - r inside, the bound outside
+// c = d y / d s^ (straight-through): q - r inside, the bound outside.  Outside
+// the range q is the clamped grid value, which is that bound (the bounds lie
+// on the grid and q takes the sign of r), so c = q - (inside ? r : 0) with no
+// branch.
 __device__ __forceinline__ float ste_c(const Elem& e, float qmin, float qmax) {
-    return e.inside ? (e.q - e.r) : (e.r > qmax ? qmax : qmin);
+    (void)qmin;
+    (void)qmax;
+    return e.q - (e.inside ? e.r : 0.0f);
 }
 
 // code of one element (4-bit value in the low bits, or 8-bit)
