@@ -48,7 +48,7 @@
 #define GEMM_SPREAD 0       // 1: spread a step's loads over the previous step's MFMAs (measured slower)
 #endif
 #ifndef GEMM_SCHED
-#define GEMM_SCHED 1        // interleave fragment reads with MFMAs explicitly
+#define GEMM_SCHED 2        // 2: per sub-step the next reads, then the MFMAs; 1, 3: interleaved
 #endif
 
 namespace fq {
@@ -342,12 +342,33 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
                                                                               0, 0, 0);
             }
         }
-        if (GEMM_SCHED) {
+        constexpr int NR = WTM * (std::is_same<ATile, KTile<BM, BK, NW>>::value ? 1 : 2) +
+                           WTN * (std::is_same<BTile, KTile<BN, BK, NW>>::value ? 1 : 2);
+        constexpr int NM = WTM * WTN;
+        if (GEMM_SCHED == 2) {
+            // each sub-step: the next sub-step's reads first, then its MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+            for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+        } else if (GEMM_SCHED == 3) {
+            // each sub-step: its MFMAs alternating with the next sub-step's reads
+            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+            for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+#pragma unroll
+                for (int r = 0; r < NM; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+        } else if (GEMM_SCHED) {
             // sub-step 0 reads, then each sub-step's MFMAs interleaved with the
             // next sub-step's reads (a row-contiguous fragment is two reads)
-            constexpr int NR = WTM * (std::is_same<ATile, KTile<BM, BK, NW>>::value ? 1 : 2) +
-                               WTN * (std::is_same<BTile, KTile<BN, BK, NW>>::value ? 1 : 2);
-            constexpr int NM = WTM * WTN;
             __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
             if (GEMM_SPREAD) __builtin_amdgcn_sched_group_barrier(0x020, LPS, 0);
 #pragma unroll
