@@ -44,9 +44,6 @@
 #define GEMM_WVM 2          // waves of the large tile along rows x columns
 #define GEMM_WVN 4
 #endif
-#ifndef GEMM_SPREAD
-#define GEMM_SPREAD 0       // 1: spread a step's loads over the previous step's MFMAs (measured slower)
-#endif
 #ifndef GEMM_SCHED
 #define GEMM_SCHED 2        // 2: per sub-step the next reads, then the MFMAs; 1, 3: interleaved
 #endif
@@ -109,12 +106,6 @@ struct KTile {
         for (int i = 0; i < PER_WAVE; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + w) * 1024, 16, voff[i], k0 * 2, 0, 0);
     }
-    // load i of the step at k0; with `valid` false an out-of-range offset
-    // (the resource holds at most 0xFFFFFFF0 bytes) writes zeros and reads nothing
-    __device__ __forceinline__ void issue_one(lds_t* tile, int k0, int i, bool valid) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + wave_id()) * 1024, 16,
-                                                 valid ? voff[i] : 0xFFFFFFF0u, valid ? k0 * 2 : 0, 0, 0);
-    }
     // fragment of the 32x32x16 MFMA: row `row0 + lane%32`, k = 16 kk + 8 (lane/32) .. +7
     __device__ static __forceinline__ bf16x8 frag(const lds_t* tile, int row0, int kk) {
         const int lane = threadIdx.x & 63;
@@ -157,10 +148,6 @@ struct MNTile {
         for (int i = 0; i < PER_WAVE; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + w) * 1024, 16,
                                                      voff[i] + (uint32_t)k0 * ld2, 0, 0, 0);
-    }
-    __device__ __forceinline__ void issue_one(lds_t* tile, int k0, int i, bool valid) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + wave_id()) * 1024, 16,
-                                                 valid ? voff[i] + (uint32_t)k0 * ld2 : 0xFFFFFFF0u, 0, 0, 0);
     }
     __device__ static __forceinline__ bf16x8 frag(const lds_t* tile, int row0, int kk) {
         const int lane = threadIdx.x & 63;
@@ -306,15 +293,9 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
 
     // MFMAs of one BK-deep step: fragments of the next 16-deep sub-step are
     // read while the current sub-step's MFMAs run.
-    // The loads of step `kl` (into stage kl) are spread over the sub-steps,
-    // LPS per sub-step, so the wave's memory instructions do not queue up
-    // behind the barrier; `lv` false issues them out of range (zeros, no reads).
-    constexpr int NS = BK / 16, LA = ATile::PER_WAVE, LPS = LOADS / NS;
-    static_assert(LOADS % NS == 0, "loads per sub-step");
-    auto compute = [&](const lds_t* st, int kl, bool lv) {
+    auto compute = [&](const lds_t* st) {
         const lds_t* sa = st;
         const lds_t* sb = st + A_BYTES;
-        lds_t* dst = smem + (kl % S) * STAGE;
         bf16x8 af[2][WTM], bfr[2][WTN];
 #pragma unroll
         for (int kk = 0; kk <= BK / 16; ++kk) {
@@ -323,14 +304,6 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
                 for (int t = 0; t < WTM; ++t) af[kk & 1][t] = ATile::frag(sa, wm * 32 * WTM + t * 32, kk);
 #pragma unroll
                 for (int t = 0; t < WTN; ++t) bfr[kk & 1][t] = BTile::frag(sb, wn * 32 * WTN + t * 32, kk);
-                if (GEMM_SPREAD) {
-#pragma unroll
-                    for (int u = 0; u < LPS; ++u) {
-                        const int q = kk * LPS + u;
-                        if (q < LA) la.issue_one(dst, kl * BK, q, lv);
-                        else lb.issue_one(dst + A_BYTES, kl * BK, q - LA, lv);
-                    }
-                }
             }
             if (kk > 0) {
                 const int s = (kk - 1) & 1;
@@ -370,14 +343,12 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             // sub-step 0 reads, then each sub-step's MFMAs interleaved with the
             // next sub-step's reads (a row-contiguous fragment is two reads)
             __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-            if (GEMM_SPREAD) __builtin_amdgcn_sched_group_barrier(0x020, LPS, 0);
 #pragma unroll
             for (int kk = 0; kk < BK / 16 - 1; ++kk) {
 #pragma unroll
                 for (int r = 0; r < NR; ++r) {
                     __builtin_amdgcn_sched_group_barrier(0x008, NM / NR > 0 ? NM / NR : 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    if (GEMM_SPREAD && r < LPS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 }
             }
             __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
@@ -407,12 +378,8 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             }
             __syncthreads();
             // the stage step kt+S-1 overwrites was read in step kt-1, finished by every wave
-            if (GEMM_SPREAD) {
-                compute(stage(kt), kt + S - 1, kt + S - 1 < nk);
-            } else {
-                if (kt + S - 1 < nk) issue(kt + S - 1);
-                compute(stage(kt), 0, false);
-            }
+            if (kt + S - 1 < nk) issue(kt + S - 1);
+            compute(stage(kt));
         }
     };
 
