@@ -19,6 +19,8 @@
  *     and nothing is read back to the host.
  *   - Every call returns an fq_status.  Arguments are validated on the host
  *     before any HIP call; on a validation error nothing is launched.
+ *   - A saved or workspace buffer belongs to one call at a time: calls that
+ *     share one must be ordered (same stream, or synchronised).
  *   - Gradients are overwritten, never accumulated.  Results are bitwise
  *     deterministic for fixed inputs (no floating-point atomics).
  *   - Device data are not checked: routing ids must lie in [0, E) and be

@@ -541,8 +541,18 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float den = 1.0f + exp_neg(g[i]);
-                sg[i] = 1.0f / den;                          // sigmoid(g)
-                h[i] = (g[i] / den) * u[i];
+                const float inv = 1.0f / den;                // sigmoid(g), correctly rounded
+                sg[i] = inv;
+                // g / den correctly rounded, as the forward forms it: from the
+                // reciprocal by the corrected division while den <= 2^120
+                float sl;
+                if (den <= 0x1p120f) {
+                    const float q0 = g[i] * inv;
+                    sl = __builtin_fmaf(__builtin_fmaf(-q0, den, g[i]), inv, q0);
+                } else {
+                    sl = g[i] / den;
+                }
+                h[i] = sl * u[i];
             }
             if (recompute) {
                 float hq[8];

@@ -220,6 +220,23 @@ def test_layer_largest_hidden_and_intermediate(H, I):
     _full_parity(L, data, P, Po, end_to_end=False)
 
 
+def test_w8a8_weight_scale_gradients_without_dx():
+    # forward + weight-scale gradients only: no dX and no routing-weight gradient
+    # requested, so the data gradient of fc1 and the unpermute are skipped
+    L, data, P, Po = _case("w8a8", 8, 256, 256, 300, 3, routing_kind="uniform", seed=19)
+    dl = DeviceLayer(L, data, P)
+    dl.forward()
+    dl.backward(dx=False, dw=False)
+    torch().cuda.synchronize()
+    S = OL.forward(L, Po, data["X"], data["ids"], data["w"])
+    check_gemm(_y(dl), S["y"], "y")
+    G = OL.backward(L, Po, S, data["dY"], data["w"])
+    for n in ("ds_w1", "ds_w2"):
+        got, ref = _g(dl, n), G[n]
+        err = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+        assert err <= 2e-3, f"{n} end-to-end norm-wise relative error {err:.2e}"
+
+
 def test_layer_empty_expert_and_single_expert():
     L, data, P, Po = _case("nvfp4", 8, 256, 128, 200, 1, seed=5)
     data["ids"][:] = 3                           # every token to expert 3; the others empty
