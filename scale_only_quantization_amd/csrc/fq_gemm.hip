@@ -18,7 +18,7 @@
 // its MFMAs.
 //   K-contiguous operand: LDS [rows][BK], the 16-B chunk index XORed with a
 //     row swizzle; a fragment (8 consecutive k of one row) is one
-//     ds_read_b128, and 8 consecutive rows at one chunk cover all banks.
+//     ds_read_b128, and the 16 rows of one read pass fall on distinct banks.
 //   Row-contiguous operand: LDS [BK][rows] as in memory, the 16-B chunk index
 //     XOR 4 (k & 3), so the 32 lanes of one ds_read_b64_tr_b16 pass (4 k-rows
 //     x 64 B) fall on distinct banks; a fragment is two such reads: inside each group
