@@ -197,3 +197,39 @@ def test_fq_tensor_full_weight_stack_sampled(q):
                                 None if t is None else t[sl], terms=ref)
         guard = codec._reduce_to_scale(q, np.abs(G[sl] * ref["c"] * ref["dfac"]), 1, 768, 2048)
         check_scale_grad(from_dev(gs[sl]), gsr, guard, f"expert {e} grad_scale")
+
+
+@pytest.mark.parametrize("q", [OP.NVFP4_A, OP.INT8_TOKEN, OP.NVFP4_W], ids=["nvfp4_dyn", "int8_token", "nvfp4_w"])
+def test_fq_tensor_zero_effective_scale(q):
+    """A zero effective scale: an all-zero dynamic block or row (amax 0), or a
+    learnable NVFP4 block scale whose E4M3 factor underflows to zero.  Such
+    elements quantise to a signed zero, their gradient passes and they add
+    nothing to the scale gradient."""
+    F = _F()
+    T = torch()
+    x, s, t = _inputs(q, (2, 12, 256), 400)
+    x[0, 1, :] = 0.0                                   # whole row of +0
+    x[0, 2, 16:48] = -0.0                              # two blocks of -0
+    x[1, 3, 64:80] = 0.0
+    if s is not None:
+        s[1, 4, 2:6] = np.float32(1e-12) * t[1]        # d = E4M3(s / t) underflows to 0
+    xd, sd, td, y, codes, bcodes = _run_fwd(q, x, s, t)
+    ref = codec.fake_quant(q, x, s, t)
+    assert_bits_equal(y, ref["y"], "y")
+    assert_array_equal(codes, ref["codes"], "codes")
+    if bcodes is not None:
+        assert_array_equal(bcodes, ref["block_codes"], "block codes")
+    g = nm.bf16_rne(np.random.default_rng(8).standard_normal(x.shape)).astype(np.float32)
+    gd = to_dev_bf16(g)
+    gx = T.empty_like(xd)
+    gxr, gsr = codec.backward(q, x, g.astype(np.float64), s, t, terms=ref)
+    gs = T.zeros(gsr.shape, dtype=T.float32, device="cuda") if q.has_param() else None
+    wsb = F.fq_tensor_workspace_size(qdesc_of(q), *x.shape)
+    ws = T.empty(max(wsb // 4, 1), dtype=T.float32, device="cuda")
+    F.fq_tensor(qdesc_of(q), xd, sd, td, grad_y=gd, grad_x=gx, grad_scale=gs, workspace=ws)
+    T.cuda.synchronize()
+    assert_bits_equal(from_dev(gx), nm.bf16_rne(gxr), "grad_x")
+    if gs is not None:
+        B, R, C = x.shape
+        guard = codec._reduce_to_scale(q, np.abs(g * ref["c"] * ref["dfac"]), B, R, C)
+        check_scale_grad(from_dev(gs), gsr, guard, "grad_scale")
