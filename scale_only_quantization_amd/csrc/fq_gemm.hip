@@ -44,6 +44,13 @@
 #define GEMM_WVM 2          // waves of the large tile along rows x columns
 #define GEMM_WVN 4
 #endif
+#ifndef GEMM_WG_SPLIT
+#define GEMM_WG_SPLIT 0     // 1: weight gradients on 256 x 128 tiles of 4 waves, two blocks per CU
+#endif
+#ifndef GEMM_WG_BK
+#define GEMM_WG_BK 32
+#define GEMM_WG_S 3
+#endif
 #ifndef GEMM_SCHED
 #define GEMM_SCHED 2        // 2: per sub-step the next reads, then the MFMAs; 1, 3: interleaved
 #endif
@@ -262,6 +269,133 @@ __device__ __forceinline__ void sg_epilogue(const GemmArgs& g, const f32x16 (&ac
     }
 }
 
+// Frozen weights of the fused epilogue staged through LDS: each wave owns two
+// 4-KB slots, each one 32-row slice of its 64 columns (bf16), filled by direct
+// global->LDS loads so that no registers wait on them.  16-B chunks of a row
+// are XOR-swizzled by (row >> 1) & 7: the 64 lanes' 8-B reads of one column
+// group then cover all 64 banks twice, the minimum for 512 B.
+struct WStage {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t K2;                                       // bytes per weight row
+    // w0: element (row 0, column 0) of the wave's block; rows x 64 columns
+    __device__ __forceinline__ void init(const uint16_t* w0, int64_t K, int rows) {
+        rs = make_rsrc(w0, ((int64_t)(rows - 1) * K + 64) * 2);
+        K2 = (uint32_t)(K * 2);
+    }
+    // rows 32 ti .. 32 ti + 31 into `slot`: 4 wave loads of 1 KB
+    __device__ __forceinline__ void issue(lds_t* slot, int ti) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = i * 64 + lane;
+            const int r = p >> 3;
+            const int c = (p & 7) ^ ((r >> 1) & 7);            // logical chunk at this position
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, slot + i * 1024, 16,
+                                                     (uint32_t)(ti * 32 + r) * K2 + (uint32_t)c * 16, 0, 0, 0);
+        }
+    }
+    // this lane's 4 weights of chunk c (columns 8 c + 4 (lane / 32) .. +3, row lane % 32)
+    __device__ static __forceinline__ uint2 read(const lds_t* slot, int c) {
+        const int lane = threadIdx.x & 63;
+        const int r = lane & 31;
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+            slot + r * 128 + ((c ^ ((r >> 1) & 7)) << 4) + (lane >> 5) * 8);
+        return make_uint2(v.x, v.y);
+    }
+};
+
+// The epilogue above with the weights read from the wave's LDS slots: slices
+// 0 and 1 were issued before the call; slice ti + 2 refills slice ti's slot as
+// soon as slice ti's weights are in registers.  A wait on the vector memory
+// counter also covers the direct-to-LDS loads; this wave alone reads its slots.
+template <int KIND, int WTM, int WTN>
+__device__ __forceinline__ void sg_epilogue_lds(const GemmArgs& g, const f32x16 (&acc)[WTM][WTN], int e,
+                                                int i_w, int j_w, int lane, const WStage& ws, lds_t* slots) {
+    static_assert(WTN == 2 && WTM >= 2, "two 32-column tiles per wave, two slots");
+    const SgArgs& sg = g.sg;
+    const int64_t N = g.N, K = g.K;
+    const float qmin = sg.q.qmin, qmax = sg.q.qmax;
+    const int gran = sg.q.gran, group = sg.q.group;
+    const float t = KIND == K_NVFP4 ? sg.tscale[e] : 0.0f;
+    float sv[WTM][WTN][2];
+    // scales of slice ti (the loads' waits are the compiler's): the row's four
+    // 16-column blocks are one 16-B load when each block has its own scale
+    auto load_sv = [&](int ti) {
+        const int64_t wrow = (int64_t)e * N + i_w + ti * 32 + (lane & 31);
+        if (KIND == K_NVFP4 || (gran == G_GROUP && group == 16)) {
+            typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+            const f32x4u v = *reinterpret_cast<const f32x4u*>(sg.scale + wrow * (K >> 4) + (j_w >> 4));
+            sv[ti][0][0] = v.x;
+            sv[ti][0][1] = v.y;
+            sv[ti][1][0] = v.z;
+            sv[ti][1][1] = v.w;
+            return;
+        }
+        if (gran != G_GROUP) {
+            const float v = sg.scale[gran == G_ROW ? wrow : (int64_t)e];
+#pragma unroll
+            for (int tj = 0; tj < WTN; ++tj) sv[ti][tj][0] = sv[ti][tj][1] = v;
+            return;
+        }
+#pragma unroll
+        for (int tj = 0; tj < WTN; ++tj)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int j = j_w + tj * 32 + 16 * b;
+                sv[ti][tj][b] = sg.scale[wrow * (K / group) + j / group];
+            }
+    };
+    load_sv(0);
+    load_sv(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int ti = 0; ti < WTM; ++ti) {
+        lds_t* slot = slots + (ti & 1) * 4096;
+        if (ti == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slices 2 and 3 have landed
+        const int64_t wrow = (int64_t)e * N + i_w + ti * 32 + (lane & 31);
+        uint2 wv[WTN][4];
+#pragma unroll
+        for (int tj = 0; tj < WTN; ++tj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wv[tj][q] = WStage::read(slot, 4 * tj + q);
+        if (ti + 2 < WTM) {
+            load_sv(ti + 2);
+            // the slot's reads have returned before it is refilled
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            ws.issue(slot, ti + 2);
+        }
+#pragma unroll
+        for (int tj = 0; tj < WTN; ++tj) {
+            const int jt = j_w + tj * 32;
+            float p[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                float sc = sv[ti][tj][b];
+                if (KIND == K_NVFP4) sc = t * e4m3_round(fminf(sc / t, 448.0f));
+                const uint2 wa = wv[tj][2 * b], wb = wv[tj][2 * b + 1];
+                const float w8[8] = {bf_lo(wa.x), bf_hi(wa.x), bf_lo(wa.y), bf_hi(wa.y),
+                                     bf_lo(wb.x), bf_hi(wb.x), bf_lo(wb.y), bf_hi(wb.y)};
+                float g8[8];
+#pragma unroll
+                for (int v = 0; v < 8; ++v) g8[v] = acc[ti][tj][8 * b + v];
+                p[b] = sg_part8<KIND>(w8, g8, sc, qmin, qmax);
+            }
+            const float b0 = p[0] + __shfl_xor(p[0], 32);
+            const float b1 = p[1] + __shfl_xor(p[1], 32);
+            if (lane < 32) {
+                if (!sg.part32) {
+                    float* o = sg.out + wrow * (K >> 4) + (jt >> 4);
+                    o[0] = b0;
+                    o[1] = b1;
+                } else {
+                    sg.out[wrow * (K >> 5) + (jt >> 5)] = b0 + b1;
+                }
+            }
+        }
+    }
+}
+
 template <int MODE, int WVM, int WVN, int WTM, int WTN, int BK, int S>
 __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmArgs g) {
     constexpr int NW = WVM * WVN;
@@ -468,10 +602,22 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         if (slot < 0 || slot >= tiles_x) return;
         setup(slot);
         prologue(nk);
+        // the fused epilogue's weights go through the stage the next tile's
+        // first loads leave free (stage 1), two 4-KB slots per wave
+        constexpr bool LDS_EPI = S == 2 && WTN == 2 && WTM >= 2 && STAGE >= NW * 8192;
+        const int wu = wave_id();                     // wave-uniform: LDS base and resource
+        lds_t* wslots = smem + STAGE + wu * 8192;
+        WStage ws;
         for (;;) {
             zero_acc();
             mainloop(nk);
             __syncthreads();          // LDS stages free; every wave has read s_slot
+            if (LDS_EPI && g.sg.out) {
+                ws.init(g.sg.W + ((int64_t)e * g.N + i0 + (wu / WVN) * 32 * WTM) * g.K + n0 + (wu % WVN) * 32 * WTN,
+                        g.K, 32 * WTM);
+                ws.issue(wslots, 0);
+                ws.issue(wslots + 4096, 1);
+            }
             if (threadIdx.x == 0) s_slot = atomicAdd(g.wg_ctr + x, 1);
             __syncthreads();
             const int next = s_slot;
@@ -483,9 +629,15 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             }
             if (g.sg.out) {
                 const int iw = ci0 + wm * 32 * WTM, jw = cn0 + wn * 32 * WTN;
-                if (g.sg.q.kind == K_NVFP4) sg_epilogue<K_NVFP4, WTM, WTN>(g, acc, ce, iw, jw, lane);
-                else if (g.sg.q.kind == K_INT) sg_epilogue<K_INT, WTM, WTN>(g, acc, ce, iw, jw, lane);
-                else sg_epilogue<K_FP8, WTM, WTN>(g, acc, ce, iw, jw, lane);
+                if constexpr (LDS_EPI) {
+                    if (g.sg.q.kind == K_NVFP4) sg_epilogue_lds<K_NVFP4, WTM, WTN>(g, acc, ce, iw, jw, lane, ws, wslots);
+                    else if (g.sg.q.kind == K_INT) sg_epilogue_lds<K_INT, WTM, WTN>(g, acc, ce, iw, jw, lane, ws, wslots);
+                    else sg_epilogue_lds<K_FP8, WTM, WTN>(g, acc, ce, iw, jw, lane, ws, wslots);
+                } else {
+                    if (g.sg.q.kind == K_NVFP4) sg_epilogue<K_NVFP4, WTM, WTN>(g, acc, ce, iw, jw, lane);
+                    else if (g.sg.q.kind == K_INT) sg_epilogue<K_INT, WTM, WTN>(g, acc, ce, iw, jw, lane);
+                    else sg_epilogue<K_FP8, WTM, WTN>(g, acc, ce, iw, jw, lane);
+                }
             } else {
 #pragma unroll
                 for (int ti = 0; ti < WTM; ++ti) {
@@ -521,6 +673,7 @@ constexpr int BM_BIG = 32 * WTM_BIG * WVM_BIG, BN_BIG = 32 * WTN_BIG * WVN_BIG;
 static_assert(BM_BIG == 256, "the large row tile is the 256-row tile table");
 #define FQ_BIG(MODE) k_gemm<MODE, WVM_BIG, WVN_BIG, WTM_BIG, WTN_BIG, BK_BIG, S_BIG>
 #define FQ_SMALL(MODE) k_gemm<MODE, 2, 2, 2, 2, BK_SMALL, S_SMALL>
+#define FQ_WGS k_gemm<WGRAD, 2, 2, 4, 2, GEMM_WG_BK, GEMM_WG_S>
 
 // Explicit instantiations: without them the host pass does not emit every
 // launch stub for this template.
@@ -530,12 +683,15 @@ template __global__ void FQ_BIG(DGRAD)(GemmArgs);
 template __global__ void FQ_SMALL(DGRAD)(GemmArgs);
 template __global__ void FQ_BIG(WGRAD)(GemmArgs);
 template __global__ void FQ_SMALL(WGRAD)(GemmArgs);
+#if GEMM_WG_SPLIT
+template __global__ void FQ_WGS(GemmArgs);
+#endif
 
 // Large tiles where the shapes allow, 128 x 128 otherwise.
 template <int MODE>
 hipError_t launch(const GemmArgs& g, hipStream_t st) {
     const bool big_m = MODE == WGRAD ? (g.N % BM_BIG == 0) : true;
-    const bool big_n = (MODE == WGRAD ? g.K : g.N) % BN_BIG == 0;
+    const bool big_n = (MODE == WGRAD ? g.K : g.N) % (MODE == WGRAD && GEMM_WG_SPLIT ? 128 : BN_BIG) == 0;
     const int big = (big_m && big_n) ? 1 : 0;
     GemmArgs a = g;
     int64_t blocks;
@@ -554,10 +710,19 @@ hipError_t launch(const GemmArgs& g, hipStream_t st) {
         if (err == hipSuccess)
             err = big ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, FQ_BIG(MODE), 64 * WVM_BIG * WVN_BIG, 0)
                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, FQ_SMALL(MODE), 256, 0);
+#if GEMM_WG_SPLIT
+        if (err == hipSuccess && big) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, FQ_WGS, 256, 0);
+#endif
         if (err != hipSuccess) return err;
         blocks = (int64_t)(cus > 8 ? cus : 8) * (per_cu > 1 ? per_cu : 1);
     }
     blocks = (blocks + 7) / 8 * 8;       // a whole number of blocks per XCD
+#if GEMM_WG_SPLIT
+    if (MODE == WGRAD && big) {
+        hipLaunchKernelGGL((FQ_WGS), dim3((unsigned)blocks), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+#endif
     if (big) hipLaunchKernelGGL((FQ_BIG(MODE)), dim3((unsigned)blocks), dim3(64 * WVM_BIG * WVN_BIG), 0, st, a);
     else hipLaunchKernelGGL((FQ_SMALL(MODE)), dim3((unsigned)blocks), dim3(256), 0, st, a);
     return hipGetLastError();

@@ -110,19 +110,32 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
     __shared__ int32_t s_a[1024];
     __shared__ int32_t s_b[1024];
     __shared__ int32_t s_c[1024];
+    __shared__ int32_t s_part[1024];
     const int e = threadIdx.x;
-    int running = 0;
-    if (e < E) {                       // the column's total, 8 independent loads at a time
-        int b = 0;
-        for (; b + 8 <= nblk; b += 8) {
+    // P threads per expert column: thread (ce, cj) = (t % E, t / E) owns the
+    // contiguous run of blocks [b0, b1); its loads are independent, 8 at a time
+    const int P = 1024 / E;
+    const int ce = e % E, cj = e / E;
+    const bool col = cj < P;
+    const int chunk = (nblk + P - 1) / P;
+    const int b0 = min(cj * chunk, nblk), b1 = col ? min(b0 + chunk, nblk) : b0;
+    int part = 0;
+    {
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {
             int h[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) h[u] = hist[(int64_t)(b + u) * E + e];
+            for (int u = 0; u < 8; ++u) h[u] = hist[(int64_t)(b + u) * E + ce];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) running += h[u];
+            for (int u = 0; u < 8; ++u) part += h[u];
         }
-        for (; b < nblk; ++b) running += hist[(int64_t)b * E + e];
+        for (; b < b1; ++b) part += hist[(int64_t)b * E + ce];
     }
+    s_part[e] = part;
+    __syncthreads();
+    int running = 0;
+    if (e < E)
+        for (int j = 0; j < P; ++j) running += s_part[j * E + e];
     const int cnt = e < E ? running : 0;
     const int m1 = (cnt + 127) / 128, m2 = (cnt + 255) / 256;
     s_cnt[e] = cnt;
@@ -141,23 +154,14 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
         s_c[e] += vc;
         __syncthreads();
     }
-    const int off = s_a[e] - cnt;
-    const int ts1 = s_b[e] - m1, ts2 = s_c[e] - m2;
     if (e < E) {
+        const int off = s_a[e] - cnt;
         counts[e] = cnt;
         offsets[e] = off;
         if (e == E - 1) {
             offsets[E] = off + cnt;
-            t128.num_tiles[0] = ts1 + m1;
-            t256.num_tiles[0] = ts2 + m2;
-        }
-        for (int i = 0; i < m1; ++i) {
-            t128.tile_expert[ts1 + i] = e;
-            t128.tile_row0[ts1 + i] = off + i * 128;
-        }
-        for (int i = 0; i < m2; ++i) {
-            t256.tile_expert[ts2 + i] = e;
-            t256.tile_row0[ts2 + i] = off + i * 256;
+            t128.num_tiles[0] = s_b[e];
+            t256.num_tiles[0] = s_c[e];
         }
         int rank = 0;
         for (int o = 0; o < E; ++o) {
@@ -166,21 +170,38 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
         }
         order[rank] = e;
         s_ord[rank] = e;
-        // each block's first row of expert e: off + the exclusive prefix over blocks
-        int acc = off, b = 0;
-        for (; b + 8 <= nblk; b += 8) {
+    }
+    if (col) {
+        // column ce's row-tile table entries i = cj, cj + P, ...
+        const int cc = s_cnt[ce], off = s_a[ce] - cc;
+        const int n1 = (cc + 127) / 128, n2 = (cc + 255) / 256;
+        const int ts1 = s_b[ce] - n1, ts2 = s_c[ce] - n2;
+        for (int i = cj; i < n1; i += P) {
+            t128.tile_expert[ts1 + i] = ce;
+            t128.tile_row0[ts1 + i] = off + i * 128;
+        }
+        for (int i = cj; i < n2; i += P) {
+            t256.tile_expert[ts2 + i] = ce;
+            t256.tile_row0[ts2 + i] = off + i * 256;
+        }
+        // each block's first row of expert ce: off + the exclusive prefix over
+        // the earlier runs of the column, then over this run's blocks
+        int acc = off;
+        for (int j = 0; j < cj; ++j) acc += s_part[j * E + ce];
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {
             int h[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) h[u] = hist[(int64_t)(b + u) * E + e];
+            for (int u = 0; u < 8; ++u) h[u] = hist[(int64_t)(b + u) * E + ce];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                hist[(int64_t)(b + u) * E + e] = acc;
+                hist[(int64_t)(b + u) * E + ce] = acc;
                 acc += h[u];
             }
         }
-        for (; b < nblk; ++b) {
-            const int h = hist[(int64_t)b * E + e];
-            hist[(int64_t)b * E + e] = acc;
+        for (; b < b1; ++b) {
+            const int h = hist[(int64_t)b * E + ce];
+            hist[(int64_t)b * E + ce] = acc;
             acc += h;
         }
     }
@@ -188,20 +209,27 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
     // Weight-gradient work per XCD (each XCD has its own L2): experts in
     // descending count go to the least loaded XCD so far (ties: lowest XCD),
     // load = reduction steps of 64 rows + 2 for the epilogue.  One wave; lane
-    // x < 8 keeps XCD x's load and list.
+    // x < 8 keeps XCD x's load and list.  The experts come 64 at a time, one
+    // per lane, and each step reads its expert and cost from a lane register.
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         int load = 0, n = 0;
-        for (int r = 0; r < E; ++r) {
-            const int ex = s_ord[r];
-            int key = lane < 8 ? load * 8 + lane : 0x7FFFFFFF;
-            key = min(key, __shfl_xor(key, 1));
-            key = min(key, __shfl_xor(key, 2));
-            key = min(key, __shfl_xor(key, 4));
-            if (lane == (key & 7)) {
-                wg_list[lane * E + n] = ex;
-                ++n;
-                load += (s_cnt[ex] + 63) / 64 + 2;
+        for (int r0 = 0; r0 < E; r0 += 64) {
+            const int ex_l = r0 + lane < E ? s_ord[r0 + lane] : 0;
+            const int cost_l = (s_cnt[ex_l] + 63) / 64 + 2;
+            const int nr = min(64, E - r0);
+            for (int i = 0; i < nr; ++i) {
+                const int ex = __builtin_amdgcn_readlane(ex_l, i);
+                const int cost = __builtin_amdgcn_readlane(cost_l, i);
+                int key = lane < 8 ? load * 8 + lane : 0x7FFFFFFF;
+                key = min(key, __shfl_xor(key, 1));
+                key = min(key, __shfl_xor(key, 2));
+                key = min(key, __shfl_xor(key, 4));
+                if (lane == (key & 7)) {
+                    wg_list[lane * E + n] = ex;
+                    ++n;
+                    load += cost;
+                }
             }
         }
         if (lane < 8) wg_cnt[lane] = n;
@@ -356,28 +384,39 @@ __device__ __forceinline__ float exp_neg(float g) {        // e^-g as the forwar
 }
 
 // ------------------------------------------------------------- F5 SwiGLU+A2 --
-template <int KIND, int NV>
+// RW rows per wave: with RW = 2 (used when a row has 32 mod 64 vectors of 8)
+// the wave's vectors u = lane + 64 c run over both rows, row u / nvec, so no
+// lane idles on a half-filled last pass.  16-blocks and quantiser groups never
+// straddle the two rows (nvec is a multiple of the group's vector count).
+template <int KIND, int NV, int RW>
 __global__ __launch_bounds__(TPB) void k_swiglu_a2(SwigluArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int nvec = a.I >> 3;
     const float qmin = a.a2.q.qmin, qmax = a.a2.q.qmax;
     const int gl = a.a2.q.group >> 3;
-    for (int64_t r = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); r < a.R; r += (int64_t)gridDim.x * RPB) {
-        const int e = clamp_id(a.row_expert[r], a.E);
-        const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + r * 2 * (int64_t)a.I);
+    for (int64_t r0 = ((int64_t)blockIdx.x * RPB + (threadIdx.x >> 6)) * RW; r0 < a.R;
+         r0 += (int64_t)gridDim.x * RPB * RW) {
+        int ex[RW];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) ex[i] = r0 + i < a.R ? clamp_id(a.row_expert[r0 + i], a.E) : 0;
         uint4 hv[NV];
         float bm[NV];
-        float rm = 0.0f;
+        float rm[RW];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) rm[i] = 0.0f;
 #pragma unroll
         for (int c = 0; c < NV; ++c) {
-            const int v = lane + c * WAVE;
+            const int u = lane + c * WAVE;
+            const int ri = (RW == 2 && u >= nvec) ? 1 : 0;
+            const int v = u - ri * nvec;
             float h[8];
-            if (v < nvec) {
-                float g[8], u[8];
+            if (u < RW * nvec && r0 + ri < a.R) {
+                const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + (r0 + ri) * 2 * (int64_t)a.I);
+                float g[8], uu[8];
                 unpack8(zr[v], g);
-                unpack8(zr[v + nvec], u);
+                unpack8(zr[v + nvec], uu);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) h[i] = (g[i] / (1.0f + exp_neg(g[i]))) * u[i];
+                for (int i = 0; i < 8; ++i) h[i] = (g[i] / (1.0f + exp_neg(g[i]))) * uu[i];
                 hv[c] = pack8(h);
                 unpack8(hv[c], h);                       // h as stored (bf16)
             } else {
@@ -386,25 +425,35 @@ __global__ __launch_bounds__(TPB) void k_swiglu_a2(SwigluArgs a) {
                 for (int i = 0; i < 8; ++i) h[i] = 0.0f;
             }
             const float m = amax8(h);
-            rm = fmaxf(rm, m);
+#pragma unroll
+            for (int i = 0; i < RW; ++i)
+                if (ri == i) rm[i] = fmaxf(rm[i], m);
             if (KIND == K_NVFP4) bm[c] = fmaxf(m, __shfl_xor(m, 1));
             else if (KIND != K_NONE && a.a2.q.gran == G_GROUP) bm[c] = group_max(m, gl);
             else bm[c] = 0.0f;
         }
-        float row_s = 0.0f;
-        if (KIND != K_NONE && KIND != K_NVFP4 && a.a2.q.gran == G_ROW && a.a2.q.source == S_DYNAMIC)
-            row_s = wave_max(rm) / a.a2.q.qdiv;
-        uint4* dst = reinterpret_cast<uint4*>(a.hhat + r * a.I);
+        float row_s[RW];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            row_s[i] = 0.0f;
+            if (KIND != K_NONE && KIND != K_NVFP4 && a.a2.q.gran == G_ROW && a.a2.q.source == S_DYNAMIC)
+                row_s[i] = wave_max(rm[i]) / a.a2.q.qdiv;
+        }
 #pragma unroll
         for (int c = 0; c < NV; ++c) {
-            const int v = lane + c * WAVE;
-            if (v >= nvec) continue;
+            const int u = lane + c * WAVE;
+            const int ri = (RW == 2 && u >= nvec) ? 1 : 0;
+            const int v = u - ri * nvec;
+            if (u >= RW * nvec || r0 + ri >= a.R) continue;
+            uint4* dst = reinterpret_cast<uint4*>(a.hhat + (r0 + ri) * a.I);
             if (KIND == K_NONE) {
                 dst[v] = hv[c];
             } else {
                 float h[8], y[8], dfac;
                 unpack8(hv[c], h);
-                quant8<KIND>(h, act_scale<KIND>(a.a2, e, bm[c], bm[c], row_s, &dfac), qmin, qmax, y);
+                const int e = RW == 2 && ri ? ex[RW - 1] : ex[0];
+                const float rs = RW == 2 && ri ? row_s[RW - 1] : row_s[0];
+                quant8<KIND>(h, act_scale<KIND>(a.a2, e, bm[c], bm[c], rs, &dfac), qmin, qmax, y);
                 dst[v] = pack8(y);
             }
         }
@@ -510,7 +559,8 @@ __global__ __launch_bounds__(TPB) void k_permute_dy(PermuteDyArgs a) {
 }
 
 // --------------------------------------------- B4 A2 backward + SwiGLU backward --
-template <int KIND>
+// RW rows per wave as in the forward above.
+template <int KIND, int RW>
 __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int nvec = a.I >> 3;
@@ -520,15 +570,25 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
     // need the forward's codec terms; per-row/group dynamic quantisers pass
     // the gradient straight and own no parameter.
     const bool recompute = KIND == K_NVFP4 || (KIND != K_NONE && !dyn);
-    for (int64_t r = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); r < a.R; r += (int64_t)gridDim.x * RPB) {
-        const int e = clamp_id(a.row_expert[r], a.E);
-        const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + r * 2 * (int64_t)a.I);
-        const uint4* dr = reinterpret_cast<const uint4*>(a.dhh + r * a.I);
-        uint4* out = reinterpret_cast<uint4*>(a.dz1 + r * 2 * (int64_t)a.I);
-        float part_row = 0.0f;
-        for (int v0 = 0; v0 < nvec; v0 += WAVE) {
-            const int v = v0 + lane;
-            const bool act = v < nvec;
+    for (int64_t r0 = ((int64_t)blockIdx.x * RPB + (threadIdx.x >> 6)) * RW; r0 < a.R;
+         r0 += (int64_t)gridDim.x * RPB * RW) {
+        int ex[RW];
+        float part_row[RW];
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            ex[i] = r0 + i < a.R ? clamp_id(a.row_expert[r0 + i], a.E) : 0;
+            part_row[i] = 0.0f;
+        }
+        for (int u0 = 0; u0 < RW * nvec; u0 += WAVE) {
+            const int uf = u0 + lane;
+            const int ri = (RW == 2 && uf >= nvec) ? 1 : 0;
+            const int v = uf - ri * nvec;
+            const int64_t r = r0 + ri;
+            const bool act = uf < RW * nvec && r < a.R;
+            const int e = RW == 2 && ri ? ex[RW - 1] : ex[0];
+            const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + r * 2 * (int64_t)a.I);
+            const uint4* dr = reinterpret_cast<const uint4*>(a.dhh + r * a.I);
+            uint4* out = reinterpret_cast<uint4*>(a.dz1 + r * 2 * (int64_t)a.I);
             float g[8], u[8], dh[8], sg[8], h[8];
             if (act) {
                 unpack8(zr[v], g);
@@ -566,7 +626,11 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
                 const float s = act_scale<KIND>(a.a2, e, bm, bm, 0.0f, &dfac);
                 float gx[8];
                 const float part = ste8<KIND>(hq, dh, s, qmin, qmax, dyn, gx);
-                if (act) part_row = __builtin_fmaf(part, dfac, part_row);
+                if (act) {
+#pragma unroll
+                    for (int i = 0; i < RW; ++i)
+                        if (ri == i) part_row[i] = __builtin_fmaf(part, dfac, part_row[i]);
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) dh[i] = gx[i];
             }
@@ -584,8 +648,11 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
             }
         }
         if (a.rowpart) {
-            const float tot = wave_sum(part_row);
-            if (lane == 0) a.rowpart[r] = tot;
+#pragma unroll
+            for (int i = 0; i < RW; ++i) {
+                const float tot = wave_sum(part_row[i]);
+                if (lane == 0 && r0 + i < a.R) a.rowpart[r0 + i] = tot;
+            }
         }
     }
 }
@@ -658,19 +725,31 @@ __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
 }
 
 // ---------------------------------------------------- per-expert segment sum --
-__global__ __launch_bounds__(TPB) void k_segment_sum(const float* rowpart, const int32_t* offsets, float* out) {
-    __shared__ float red[TPB];
+// One block per expert; each thread adds four independent loads per step (in a
+// fixed order), then the waves' sums are combined in wave order: the result
+// depends only on the segment's length, never on timing.
+constexpr int SEG_TPB = 1024;
+__global__ __launch_bounds__(SEG_TPB) void k_segment_sum(const float* rowpart, const int32_t* offsets, float* out) {
+    __shared__ float red[SEG_TPB / WAVE];
     const int e = blockIdx.x;
     const int64_t lo = offsets[e], hi = offsets[e + 1];
     float acc = 0.0f;
-    for (int64_t r = lo + threadIdx.x; r < hi; r += TPB) acc += rowpart[r];
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    for (int w = TPB / 2; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
+    int64_t r = lo + threadIdx.x;
+    for (; r + 3 * SEG_TPB < hi; r += 4 * SEG_TPB) {
+        const float a0 = rowpart[r], a1 = rowpart[r + SEG_TPB];
+        const float a2 = rowpart[r + 2 * SEG_TPB], a3 = rowpart[r + 3 * SEG_TPB];
+        acc += (a0 + a1) + (a2 + a3);
     }
-    if (threadIdx.x == 0) out[e] = red[0];
+    for (; r < hi; r += SEG_TPB) acc += rowpart[r];
+    acc = wave_sum(acc);
+    if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < SEG_TPB / WAVE; ++w) t += red[w];
+        out[e] = t;
+    }
 }
 
 unsigned grid_waves(int64_t n) {
@@ -729,9 +808,42 @@ hipError_t launch_permute_a1(const PermuteArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// two rows per wave when a row is 32, 96, 160 or 224 vectors of 8 (then both
+// rows fill 1, 3, 5 or 7 whole passes of the wave)
+static int paired_nv(int I) {
+    const int nvec = I >> 3;
+    return (nvec % 64 == 32 && nvec <= 224) ? 2 * nvec / 64 : 0;
+}
+
+#define FQ_SWIGLU_PAIRED(KIND, NVV, GRID)                                                          \
+    switch (NVV) {                                                                                  \
+    case 1: hipLaunchKernelGGL((k_swiglu_a2<KIND, 1, 2>), GRID, dim3(TPB), 0, st, a); break;        \
+    case 3: hipLaunchKernelGGL((k_swiglu_a2<KIND, 3, 2>), GRID, dim3(TPB), 0, st, a); break;        \
+    case 5: hipLaunchKernelGGL((k_swiglu_a2<KIND, 5, 2>), GRID, dim3(TPB), 0, st, a); break;        \
+    default: hipLaunchKernelGGL((k_swiglu_a2<KIND, 7, 2>), GRID, dim3(TPB), 0, st, a); break;       \
+    }
+#define FQ_SWIGLU_SINGLE(KIND, NVV, GRID)                                                          \
+    switch (NVV) {                                                                                  \
+    case 2: hipLaunchKernelGGL((k_swiglu_a2<KIND, 2, 1>), GRID, dim3(TPB), 0, st, a); break;        \
+    case 4: hipLaunchKernelGGL((k_swiglu_a2<KIND, 4, 1>), GRID, dim3(TPB), 0, st, a); break;        \
+    case 8: hipLaunchKernelGGL((k_swiglu_a2<KIND, 8, 1>), GRID, dim3(TPB), 0, st, a); break;        \
+    default: hipLaunchKernelGGL((k_swiglu_a2<KIND, 16, 1>), GRID, dim3(TPB), 0, st, a); break;      \
+    }
+
 hipError_t launch_swiglu_a2(const SwigluArgs& a, hipStream_t st) {
     if (a.R == 0) return hipSuccess;
-    FQ_KIND_NV_SWITCH(a.a2.q.kind, nv_for(a.I), k_swiglu_a2, dim3(grid_waves(a.R)), a);
+    const int pnv = paired_nv(a.I);
+    const dim3 grid(grid_waves(pnv ? (a.R + 1) / 2 : a.R));
+#define FQ_SWIGLU_FWD(KIND)                                                                         \
+    if (pnv) { FQ_SWIGLU_PAIRED(KIND, pnv, grid) }                                                  \
+    else { FQ_SWIGLU_SINGLE(KIND, nv_for(a.I), grid) }
+    switch (a.a2.q.kind) {
+    case K_NONE: FQ_SWIGLU_FWD(K_NONE); break;
+    case K_NVFP4: FQ_SWIGLU_FWD(K_NVFP4); break;
+    case K_INT: FQ_SWIGLU_FWD(K_INT); break;
+    default: FQ_SWIGLU_FWD(K_FP8); break;
+    }
+#undef FQ_SWIGLU_FWD
     return hipGetLastError();
 }
 
@@ -761,13 +873,18 @@ hipError_t launch_permute_dy(const PermuteDyArgs& a, hipStream_t st) {
 
 hipError_t launch_swiglu_bwd(const SwigluBwdArgs& a, hipStream_t st) {
     if (a.R == 0) return hipSuccess;
-    const dim3 grid(grid_waves(a.R));
+    const bool paired = ((a.I >> 3) % 64) == 32;
+    const dim3 grid(grid_waves(paired ? (a.R + 1) / 2 : a.R));
+#define FQ_SWIGLU_BWD(KIND)                                                                         \
+    if (paired) hipLaunchKernelGGL((k_swiglu_bwd<KIND, 2>), grid, dim3(TPB), 0, st, a);             \
+    else hipLaunchKernelGGL((k_swiglu_bwd<KIND, 1>), grid, dim3(TPB), 0, st, a);
     switch (a.a2.q.kind) {
-    case K_NONE: hipLaunchKernelGGL(k_swiglu_bwd<K_NONE>, grid, dim3(TPB), 0, st, a); break;
-    case K_NVFP4: hipLaunchKernelGGL(k_swiglu_bwd<K_NVFP4>, grid, dim3(TPB), 0, st, a); break;
-    case K_INT: hipLaunchKernelGGL(k_swiglu_bwd<K_INT>, grid, dim3(TPB), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_swiglu_bwd<K_FP8>, grid, dim3(TPB), 0, st, a); break;
+    case K_NONE: FQ_SWIGLU_BWD(K_NONE); break;
+    case K_NVFP4: FQ_SWIGLU_BWD(K_NVFP4); break;
+    case K_INT: FQ_SWIGLU_BWD(K_INT); break;
+    default: FQ_SWIGLU_BWD(K_FP8); break;
     }
+#undef FQ_SWIGLU_BWD
     return hipGetLastError();
 }
 
@@ -779,7 +896,7 @@ hipError_t launch_unpermute_a1(const UnpermuteArgs& a, hipStream_t st) {
 
 hipError_t launch_segment_sum(const float* rowpart, const int32_t* offsets, int E, float* out,
                               hipStream_t st) {
-    hipLaunchKernelGGL(k_segment_sum, dim3((unsigned)E), dim3(TPB), 0, st, rowpart, offsets, out);
+    hipLaunchKernelGGL(k_segment_sum, dim3((unsigned)E), dim3(SEG_TPB), 0, st, rowpart, offsets, out);
     return hipGetLastError();
 }
 

@@ -213,6 +213,15 @@ def test_layer_ragged_tiles_and_wide_hidden():
     _full_parity(L, data, P, Po)
 
 
+@pytest.mark.parametrize("fmt,I", [("nvfp4", 768), ("w8a8", 768), ("fp8", 768), ("nvfp4", 256)],
+                         ids=["nvfp4-768", "w8a8-768", "fp8-768", "nvfp4-256"])
+def test_layer_two_rows_per_wave(fmt, I):
+    # a row of 96 (or 32) vectors of 8 puts two rows in each wave of the SwiGLU
+    # kernels; 37 tokens x top-3 = 111 rows leaves the last wave a single row
+    L, data, P, Po = _case(fmt, 4, 256, I, 37, 3, routing_kind="zipf", seed=23)
+    _full_parity(L, data, P, Po)
+
+
 @pytest.mark.parametrize("H,I", [(8192, 256), (256, 8192)], ids=["hidden8192", "intermediate8192"])
 def test_layer_largest_hidden_and_intermediate(H, I):
     # the largest widths the library accepts (16 vectors of 8 per lane per row)
