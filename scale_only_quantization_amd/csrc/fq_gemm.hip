@@ -44,13 +44,6 @@
 #define GEMM_WVM 2          // waves of the large tile along rows x columns
 #define GEMM_WVN 4
 #endif
-#ifndef GEMM_WG_SPLIT
-#define GEMM_WG_SPLIT 0     // 1: weight gradients on 256 x 128 tiles of 4 waves, two blocks per CU
-#endif
-#ifndef GEMM_WG_BK
-#define GEMM_WG_BK 32
-#define GEMM_WG_S 3
-#endif
 #ifndef GEMM_SCHED
 #define GEMM_SCHED 2        // 2: per sub-step the next reads, then the MFMAs; 1, 3: interleaved
 #endif
@@ -673,7 +666,6 @@ constexpr int BM_BIG = 32 * WTM_BIG * WVM_BIG, BN_BIG = 32 * WTN_BIG * WVN_BIG;
 static_assert(BM_BIG == 256, "the large row tile is the 256-row tile table");
 #define FQ_BIG(MODE) k_gemm<MODE, WVM_BIG, WVN_BIG, WTM_BIG, WTN_BIG, BK_BIG, S_BIG>
 #define FQ_SMALL(MODE) k_gemm<MODE, 2, 2, 2, 2, BK_SMALL, S_SMALL>
-#define FQ_WGS k_gemm<WGRAD, 2, 2, 4, 2, GEMM_WG_BK, GEMM_WG_S>
 
 // Explicit instantiations: without them the host pass does not emit every
 // launch stub for this template.
@@ -683,15 +675,12 @@ template __global__ void FQ_BIG(DGRAD)(GemmArgs);
 template __global__ void FQ_SMALL(DGRAD)(GemmArgs);
 template __global__ void FQ_BIG(WGRAD)(GemmArgs);
 template __global__ void FQ_SMALL(WGRAD)(GemmArgs);
-#if GEMM_WG_SPLIT
-template __global__ void FQ_WGS(GemmArgs);
-#endif
 
 // Large tiles where the shapes allow, 128 x 128 otherwise.
 template <int MODE>
 hipError_t launch(const GemmArgs& g, hipStream_t st) {
     const bool big_m = MODE == WGRAD ? (g.N % BM_BIG == 0) : true;
-    const bool big_n = (MODE == WGRAD ? g.K : g.N) % (MODE == WGRAD && GEMM_WG_SPLIT ? 128 : BN_BIG) == 0;
+    const bool big_n = (MODE == WGRAD ? g.K : g.N) % BN_BIG == 0;
     const int big = (big_m && big_n) ? 1 : 0;
     GemmArgs a = g;
     int64_t blocks;
@@ -710,19 +699,10 @@ hipError_t launch(const GemmArgs& g, hipStream_t st) {
         if (err == hipSuccess)
             err = big ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, FQ_BIG(MODE), 64 * WVM_BIG * WVN_BIG, 0)
                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, FQ_SMALL(MODE), 256, 0);
-#if GEMM_WG_SPLIT
-        if (err == hipSuccess && big) err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, FQ_WGS, 256, 0);
-#endif
         if (err != hipSuccess) return err;
         blocks = (int64_t)(cus > 8 ? cus : 8) * (per_cu > 1 ? per_cu : 1);
     }
     blocks = (blocks + 7) / 8 * 8;       // a whole number of blocks per XCD
-#if GEMM_WG_SPLIT
-    if (MODE == WGRAD && big) {
-        hipLaunchKernelGGL((FQ_WGS), dim3((unsigned)blocks), dim3(256), 0, st, a);
-        return hipGetLastError();
-    }
-#endif
     if (big) hipLaunchKernelGGL((FQ_BIG(MODE)), dim3((unsigned)blocks), dim3(64 * WVM_BIG * WVN_BIG), 0, st, a);
     else hipLaunchKernelGGL((FQ_SMALL(MODE)), dim3((unsigned)blocks), dim3(256), 0, st, a);
     return hipGetLastError();
