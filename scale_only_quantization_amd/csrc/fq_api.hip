@@ -174,7 +174,7 @@ Layout layout(const fq_layer_desc* L, const LayerQ& q) {
     place(y.dw2, q.w2.kind != FQ_NONE && m2 == 0 ? (size_t)E * H * I * 4 : 0, c);
     place(y.sgp1, m1 == 2 ? (size_t)E * 2 * I * (H / 32) * 4 : 0, c);
     place(y.sgp2, m2 == 2 ? (size_t)E * H * (I / 32) * 4 : 0, c);
-    place(y.rowpart1, R * 4, c);
+    place(y.rowpart1, R * 4 * unpermute_split((int)L->H), c);
     place(y.rowpart2, R * 4, c);
     const size_t t1 = tensor_workspace_bytes(q.w1, E, 2 * I);
     const size_t t2 = tensor_workspace_bytes(q.w2, E, H);
@@ -646,7 +646,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
     FQ_TRY(mark(events, 3, st));
     FQ_TRY(launch_swiglu_bwd(sb, st));
     FQ_TRY(mark(events, 4, st));
-    if (G->ds_a2) FQ_TRY(launch_segment_sum(sb.rowpart, offsets, E, G->ds_a2, st));
+    if (G->ds_a2) FQ_TRY(launch_segment_sum(sb.rowpart, offsets, E, 1, G->ds_a2, st));
     FQ_TRY(mark(events, 5, st));
 
     const bool need_dxh = dx || G->ds_a1;
@@ -697,7 +697,7 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         ua.a1 = ActQ{q.a1, P->s_a1};
         FQ_TRY(launch_unpermute_a1(ua, st));
         FQ_TRY(mark(events, 8, st));
-        if (G->ds_a1) FQ_TRY(launch_segment_sum(ua.rowpart, offsets, E, G->ds_a1, st));
+        if (G->ds_a1) FQ_TRY(launch_segment_sum(ua.rowpart, offsets, E, unpermute_split((int)L->H), G->ds_a1, st));
     }
 
     if (!need_dxh) FQ_TRY(mark(events, 8, st));

@@ -137,9 +137,12 @@ struct UnpermuteArgs {     // dX[t] = sum_j mask * dXhat[row]; per-row partial o
     ActQ a1;
 };
 hipError_t launch_unpermute_a1(const UnpermuteArgs& a, hipStream_t st);
+// partials of ds_a1 the unpermute writes per routed row (its waves per token)
+int unpermute_split(int H);
 
-// ds[e] = sum of rowpart over rows [offsets[e], offsets[e+1]) in a fixed order
-hipError_t launch_segment_sum(const float* rowpart, const int32_t* offsets, int E,
+// ds[e] = sum of the `per` partials of each row in [offsets[e], offsets[e+1]),
+// in a fixed order
+hipError_t launch_segment_sum(const float* rowpart, const int32_t* offsets, int E, int per,
                               float* out, hipStream_t st);
 
 // ------------------------------------------------------------------ GEMMs ---

@@ -658,21 +658,30 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
 }
 
 // ------------------------------------------- B7 A1 backward + unpermute-sum --
-template <int KIND, int NV>
+// SPLIT waves per token, each on a contiguous 1/SPLIT of the row: the recomputed
+// codec terms depend only on 16-blocks or a per-expert scale, never on the
+// whole row, and half rows keep the wave's registers (and occupancy) in bounds.
+// The per-row partial of ds_a1 is then SPLIT partials, rowpart[row SPLIT + half].
+template <int KIND, int NV, int SPLIT>
 __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
-    const int nvec = a.H >> 3;
+    const int nvl = (a.H >> 3) / SPLIT;          // vectors of 8 in this wave's part of the row
     const float qmin = a.a1.q.qmin, qmax = a.a1.q.qmax;
     const bool dyn = a.a1.q.source == S_DYNAMIC;
     const bool recompute = KIND == K_NVFP4 || (KIND != K_NONE && !dyn);
-    for (int64_t t = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); t < a.T; t += (int64_t)gridDim.x * RPB) {
+    for (int64_t w = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); w < a.T * SPLIT;
+         w += (int64_t)gridDim.x * RPB) {
+        const int64_t t = w / SPLIT;
+        const int hf = (int)(w - t * SPLIT);
+        const int nvec = nvl;                    // the loops below see only this part
+        const uint16_t* xrow = a.x + t * a.H + hf * nvl * 8;
         uint4 xv[NV];
         float bm[NV];
         if (recompute) {
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
                 const int v = lane + c * WAVE;
-                xv[c] = v < nvec ? reinterpret_cast<const uint4*>(a.x + t * a.H)[v] : make_uint4(0, 0, 0, 0);
+                xv[c] = v < nvec ? reinterpret_cast<const uint4*>(xrow)[v] : make_uint4(0, 0, 0, 0);
                 float f[8];
                 unpack8(xv[c], f);
                 const float m = amax8(f);
@@ -688,7 +697,7 @@ __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
         for (int j = 0; j < a.k; ++j) {
             const int e = slot_i(sl.e, j);
             const int64_t row = slot_i(sl.row, j);
-            const uint4* src = reinterpret_cast<const uint4*>(a.dxh + row * a.H);
+            const uint4* src = reinterpret_cast<const uint4*>(a.dxh + row * a.H + hf * nvl * 8);
             float part_row = 0.0f;
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
@@ -711,14 +720,14 @@ __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
             }
             if (a.rowpart) {
                 const float tot = wave_sum(part_row);
-                if (lane == 0) a.rowpart[row] = tot;
+                if (lane == 0) a.rowpart[row * SPLIT + hf] = tot;
             }
         }
         if (a.dx) {
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
                 const int v = lane + c * WAVE;
-                if (v < nvec) reinterpret_cast<uint4*>(a.dx + t * a.H)[v] = pack8(acc[c]);
+                if (v < nvec) reinterpret_cast<uint4*>(a.dx + t * a.H + hf * nvl * 8)[v] = pack8(acc[c]);
             }
         }
     }
@@ -729,10 +738,11 @@ __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
 // fixed order), then the waves' sums are combined in wave order: the result
 // depends only on the segment's length, never on timing.
 constexpr int SEG_TPB = 1024;
-__global__ __launch_bounds__(SEG_TPB) void k_segment_sum(const float* rowpart, const int32_t* offsets, float* out) {
+__global__ __launch_bounds__(SEG_TPB) void k_segment_sum(const float* rowpart, const int32_t* offsets, int per,
+                                                      float* out) {
     __shared__ float red[SEG_TPB / WAVE];
     const int e = blockIdx.x;
-    const int64_t lo = offsets[e], hi = offsets[e + 1];
+    const int64_t lo = (int64_t)offsets[e] * per, hi = (int64_t)offsets[e + 1] * per;
     float acc = 0.0f;
     int64_t r = lo + threadIdx.x;
     for (; r + 3 * SEG_TPB < hi; r += 4 * SEG_TPB) {
@@ -888,15 +898,44 @@ hipError_t launch_swiglu_bwd(const SwigluBwdArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+int unpermute_split(int H) {
+    const int nvec = H >> 3;
+    return (nvec % 128 == 0 && nvec >= 256) ? 2 : 1;
+}
+
 hipError_t launch_unpermute_a1(const UnpermuteArgs& a, hipStream_t st) {
     if (a.T == 0) return hipSuccess;
-    FQ_KIND_NV_SWITCH(a.a1.q.kind, nv_for(a.H), k_unpermute_a1, dim3(grid_waves(a.T)), a);
+    const int split = unpermute_split(a.H);
+    const dim3 grid(grid_waves(a.T * split));
+    const int nv = nv_for(a.H / split);
+#define FQ_UNPERM(KIND)                                                                                 \
+    if (split == 2) {                                                                                   \
+        switch (nv) {                                                                                   \
+        case 2: hipLaunchKernelGGL((k_unpermute_a1<KIND, 2, 2>), grid, dim3(TPB), 0, st, a); break;     \
+        case 4: hipLaunchKernelGGL((k_unpermute_a1<KIND, 4, 2>), grid, dim3(TPB), 0, st, a); break;     \
+        default: hipLaunchKernelGGL((k_unpermute_a1<KIND, 8, 2>), grid, dim3(TPB), 0, st, a); break;    \
+        }                                                                                               \
+    } else {                                                                                            \
+        switch (nv) {                                                                                   \
+        case 2: hipLaunchKernelGGL((k_unpermute_a1<KIND, 2, 1>), grid, dim3(TPB), 0, st, a); break;     \
+        case 4: hipLaunchKernelGGL((k_unpermute_a1<KIND, 4, 1>), grid, dim3(TPB), 0, st, a); break;     \
+        case 8: hipLaunchKernelGGL((k_unpermute_a1<KIND, 8, 1>), grid, dim3(TPB), 0, st, a); break;     \
+        default: hipLaunchKernelGGL((k_unpermute_a1<KIND, 16, 1>), grid, dim3(TPB), 0, st, a); break;  \
+        }                                                                                               \
+    }
+    switch (a.a1.q.kind) {
+    case K_NONE: FQ_UNPERM(K_NONE); break;
+    case K_NVFP4: FQ_UNPERM(K_NVFP4); break;
+    case K_INT: FQ_UNPERM(K_INT); break;
+    default: FQ_UNPERM(K_FP8); break;
+    }
+#undef FQ_UNPERM
     return hipGetLastError();
 }
 
-hipError_t launch_segment_sum(const float* rowpart, const int32_t* offsets, int E, float* out,
+hipError_t launch_segment_sum(const float* rowpart, const int32_t* offsets, int E, int per, float* out,
                               hipStream_t st) {
-    hipLaunchKernelGGL(k_segment_sum, dim3((unsigned)E), dim3(SEG_TPB), 0, st, rowpart, offsets, out);
+    hipLaunchKernelGGL(k_segment_sum, dim3((unsigned)E), dim3(SEG_TPB), 0, st, rowpart, offsets, per, out);
     return hipGetLastError();
 }
 
