@@ -563,7 +563,8 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             const int64_t r = m0 + row;
             const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
                 smem + row * RB + ((c ^ (row & 15)) << 4));
-            if (r < m_end) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.C) + r * g.ldc + n0 + c * 8) = v;
+            // streaming (non-temporal) stores: the output is next read by another kernel
+            if (r < m_end) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.C) + r * g.ldc + n0 + c * 8));
         }
     } else {
         // Persistent: the blocks of XCD group x = blockIdx % 8 (dealt to XCD x)
