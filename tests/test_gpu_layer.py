@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import codec, layer as OL, routing
+from oracle import codec, layer as OL, presets as OP, routing
+from oracle.codec import QSpec
 from oracle.numerics import F32, bf16_rne
 from tests.fq_testutil import (assert_array_equal, assert_bits_equal, check_gemm, check_scale_grad,
                                torch)
@@ -61,8 +62,9 @@ def _full_parity(L, data, P, Po, end_to_end=True):
     dYr, dHh, dZ1, dXh = dl.read("dyr"), dl.read("dhhat"), dl.read("dz1"), dl.read("dxhat")
     # dW^ reaches memory only where the weight-scale gradient is not formed in
     # the weight-gradient GEMM's epilogue
-    dW1 = dl.read("dw1hat") if L.w1.enabled and dl.F.buffer(dl.desc, "dw1hat")[1] else None
-    dW2 = dl.read("dw2hat") if L.w2.enabled and dl.F.buffer(dl.desc, "dw2hat")[1] else None
+    # dW^ is formed only for a weight quantiser with a parameter
+    dW1 = dl.read("dw1hat") if L.w1.has_param() and dl.F.buffer(dl.desc, "dw1hat")[1] else None
+    dW2 = dl.read("dw2hat") if L.w2.has_param() and dl.F.buffer(dl.desc, "dw2hat")[1] else None
     sa1, sa2 = P.get("s_a1"), P.get("s_a2")
     ds_a1_ref = np.zeros(L.E)
     ds_a2_ref = np.zeros(L.E)
@@ -227,6 +229,20 @@ def test_layer_largest_hidden_and_intermediate(H, I):
     # the largest widths the library accepts (16 vectors of 8 per lane per row)
     L, data, P, Po = _case("nvfp4", 2, H, I, 40, 2, seed=17)
     _full_parity(L, data, P, Po, end_to_end=False)
+
+
+def test_layer_dynamic_weight_quantisers():
+    # weights quantised on the fly, with no weight parameter: fc1 INT8 per row
+    # (its W^ is formed, then transposed for the data gradient) and fc2 INT4 per
+    # 32-group (fake-quant and transposed copy in one pass); 37 x 3 rows
+    case = synth.LayerCase("t", 4, 256, 256, 37, 3, "zipf", "w8a8", 29)
+    data = synth.make_layer(case)
+    _, _, a1, a2 = OP.PRESETS["w8a8"]
+    L = OL.LayerSpec(4, 256, 256, 37, 3, QSpec("int", "row", 0, "dynamic", -128, 127),
+                     QSpec("int", "group", 32, "dynamic", -8, 7), a1, a2)
+    P = dict(s_w1=None, t_w1=None, s_w2=None, t_w2=None, s_a1=None, s_a2=None)
+    Po = dict(P, W1=data["W1"], W2=data["W2"])
+    _full_parity(L, data, P, Po)
 
 
 def test_w8a8_weight_scale_gradients_without_dx():
