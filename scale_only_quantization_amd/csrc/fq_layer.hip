@@ -300,21 +300,26 @@ __device__ __forceinline__ float amax8(const float* f) {
 // One wave per token: x[t] is read once, block / row statistics formed once,
 // then each of its k routed copies is quantised with its expert's quantiser
 // and written to its row.
-template <int KIND, int NV>
+// SPLIT waves per token, each on a contiguous 1/SPLIT of the row, unless the
+// quantiser's scale is a whole-row statistic (dynamic per row).
+template <int KIND, int NV, int SPLIT>
 __global__ __launch_bounds__(TPB) void k_permute_a1(PermuteArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
-    const int nvec = a.H >> 3;
+    const int nvec = (a.H >> 3) / SPLIT;         // vectors of 8 in this wave's part of the row
     const float qmin = a.a1.q.qmin, qmax = a.a1.q.qmax;
     const int gl = a.a1.q.group >> 3;
     const bool indep = KIND != K_NONE && KIND != K_NVFP4 && a.a1.q.source == S_DYNAMIC;
-    for (int64_t t = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); t < a.T; t += (int64_t)gridDim.x * RPB) {
+    for (int64_t w = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); w < a.T * SPLIT;
+         w += (int64_t)gridDim.x * RPB) {
+        const int64_t t = w / SPLIT;
+        const int64_t c0 = (w - t * SPLIT) * nvec * 8;  // first column of this part
         uint4 xv[NV];
         float bm[NV];
         float rm = 0.0f;
 #pragma unroll
         for (int c = 0; c < NV; ++c) {
             const int v = lane + c * WAVE;
-            xv[c] = v < nvec ? reinterpret_cast<const uint4*>(a.x + t * a.H)[v] : make_uint4(0, 0, 0, 0);
+            xv[c] = v < nvec ? reinterpret_cast<const uint4*>(a.x + t * a.H + c0)[v] : make_uint4(0, 0, 0, 0);
             float f[8];
             unpack8(xv[c], f);
             const float m = amax8(f);
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(TPB) void k_permute_a1(PermuteArgs a) {
         for (int j = 0; j < a.k; ++j) {
             const int e = slot_i(sl.e, j);
             const int64_t row = slot_i(sl.row, j);
-            uint4* dst = reinterpret_cast<uint4*>(a.xhat + row * a.H);
+            uint4* dst = reinterpret_cast<uint4*>(a.xhat + row * a.H + c0);
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
                 const int v = lane + c * WAVE;
@@ -814,7 +819,33 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
 
 hipError_t launch_permute_a1(const PermuteArgs& a, hipStream_t st) {
     if (a.T == 0) return hipSuccess;
-    FQ_KIND_NV_SWITCH(a.a1.q.kind, nv_for(a.H), k_permute_a1, dim3(grid_waves(a.T)), a);
+    const bool row_stat = a.a1.q.kind != K_NONE && a.a1.q.kind != K_NVFP4 && a.a1.q.gran == G_ROW &&
+                          a.a1.q.source == S_DYNAMIC;
+    const int split = row_stat ? 1 : unpermute_split(a.H);
+    const dim3 grid(grid_waves(a.T * split));
+    const int nv = nv_for(a.H / split);
+#define FQ_PERM(KIND)                                                                                   \
+    if (split == 2) {                                                                                   \
+        switch (nv) {                                                                                   \
+        case 2: hipLaunchKernelGGL((k_permute_a1<KIND, 2, 2>), grid, dim3(TPB), 0, st, a); break;       \
+        case 4: hipLaunchKernelGGL((k_permute_a1<KIND, 4, 2>), grid, dim3(TPB), 0, st, a); break;       \
+        default: hipLaunchKernelGGL((k_permute_a1<KIND, 8, 2>), grid, dim3(TPB), 0, st, a); break;      \
+        }                                                                                               \
+    } else {                                                                                            \
+        switch (nv) {                                                                                   \
+        case 2: hipLaunchKernelGGL((k_permute_a1<KIND, 2, 1>), grid, dim3(TPB), 0, st, a); break;       \
+        case 4: hipLaunchKernelGGL((k_permute_a1<KIND, 4, 1>), grid, dim3(TPB), 0, st, a); break;       \
+        case 8: hipLaunchKernelGGL((k_permute_a1<KIND, 8, 1>), grid, dim3(TPB), 0, st, a); break;       \
+        default: hipLaunchKernelGGL((k_permute_a1<KIND, 16, 1>), grid, dim3(TPB), 0, st, a); break;    \
+        }                                                                                               \
+    }
+    switch (a.a1.q.kind) {
+    case K_NONE: FQ_PERM(K_NONE); break;
+    case K_NVFP4: FQ_PERM(K_NVFP4); break;
+    case K_INT: FQ_PERM(K_INT); break;
+    default: FQ_PERM(K_FP8); break;
+    }
+#undef FQ_PERM
     return hipGetLastError();
 }
 
