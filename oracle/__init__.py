@@ -21,6 +21,8 @@ codec     one quantiser: effective scale, quantise/dequantise, codes, and the
 routing   expert histogram, offsets and the stable permutation.
 layer     the SwiGLU expert layer forward and backward (float64 GEMMs).
 presets   the six format names mapped to four quantiser descriptors.
+optim     the scale optimiser step: AdamW with global-norm clipping and the
+          range projection of the updated scales.
 
 Precision: every codec step is IEEE float32 (numpy float32 arithmetic is
 correctly rounded); GEMMs, gradients and sums are float64.  Pure-Python loops
