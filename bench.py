@@ -158,6 +158,45 @@ def sources_sha(kernel):
     return h.hexdigest()[:16]
 
 
+def scale_adamw_step(ev, F, dl, L, reps=20, warmup=3):
+    """The scale optimiser step (fq_scale_adamw) over the layer's learnable
+    scales with the gradients of the last backward: NVFP4 block scales of both
+    stacks (projected against their tensor scales) and the activation tensor
+    scales.  Algorithmic bytes: the norm pass reads g (4 B per element), the
+    update reads p, g, m, v and writes p, m, v (28 B)."""
+    import torch
+    params, keep, count = [], [], 0
+    for n, q in (("w1", L.w1), ("w2", L.w2), ("a1", L.a1), ("a2", L.a2)):
+        g = dl.g.get("ds_" + n)
+        if g is None:
+            continue
+        p = dl.d["s_" + n]
+        m, v = torch.zeros_like(p), torch.zeros_like(p)
+        t = dl.d.get("t_" + n) if n.startswith("w") and q.kind == "nvfp4" else None
+        per = p.numel() // t.numel() if t is not None else 1
+        keep += [m, v]
+        params.append(F.scale_param(p, g, m, v, t, per))
+        count += p.numel()
+    if not params:
+        return None
+    ws = torch.empty(F.scale_adamw_workspace_size(params) // 4 + 1, dtype=torch.float32, device="cuda")
+    hp = F.adamw_defaults()
+    for i in range(warmup):
+        F.scale_adamw(params, hp, 1 + i, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = ev.create(2)
+    ev.record(e0)
+    for i in range(reps):
+        F.scale_adamw(params, hp, 1 + warmup + i, workspace=ws)
+    ev.record(e1)
+    ev.sync(e1)
+    ms = ev.elapsed_ms(e0, e1) / reps
+    alg = 32 * count
+    gbs = alg / (ms * 1e-3) / 1e9
+    return dict(ms=round(ms, 4), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 3), bytes=alg,
+                elements=count, tensors=len(params))
+
+
 def fake_quant_stack(ev, F, reps=20, warmup=3):
     """Standalone fq_tensor on the weight-only microbench stack: 128 expert
     matrices 768 x 2048 bf16 N(0, 0.02) with 0.1% outliers x 20, NVFP4 block-16
@@ -361,6 +400,9 @@ def main():
         "roofline": roof,
         "stages": stages,
     }
+    out["scale_adamw"] = scale_adamw_step(ev, F, dl, L)
+    if args.stages:
+        print(f"[bench] scale_adamw {out['scale_adamw']}", file=sys.stderr)
     del dl
     torch.cuda.empty_cache()
     print("[bench] weight-only fake-quant microbench ...", file=sys.stderr, flush=True)

@@ -272,6 +272,57 @@ typedef enum {
  * stored and reduced by the fake-quant backward. */
 int fq_grouped_expert_buffer(const fq_layer_desc* L, int32_t which, size_t* offset, size_t* bytes);
 
+/* ---- scale optimiser step --------------------------------------------------
+ * One AdamW step over the learnable quantiser scales (the only trained
+ * parameters), all gradients first clipped by their global L2 norm.  The
+ * settings are those of the AngelSlim "MCoreQAD Backend" page ("Train from
+ * YAML", the optim block: lr 2e-4, weight decay 0, betas (0.9, 0.95), grad clip
+ * 1.0; the nxmr.cn article, section 四, notes that scale-only training takes
+ * this higher rate).  The pages name no algorithm; betas with decoupled decay
+ * are read as AdamW in PyTorch's documented form (eps 1e-8):
+ *     c = min(1, max_grad_norm / (||g|| + 1e-6))     (c = 1 if max_grad_norm <= 0)
+ *     g' = c g;   m = b1 m + (1 - b1) g';   v = b2 v + (1 - b2) g'^2
+ *     p = p (1 - lr wd) - (lr / (1 - b1^step)) m / (sqrt(v) / sqrt(1 - b2^step) + eps)
+ * with ||g|| over every tensor of the call.  The updated scale is then kept
+ * usable by the forward: an NVFP4 block scale clamped into
+ * [t 2^-9, t 448] of its tensor scale t (s / t then casts to a finite,
+ * non-zero E4M3 value), any other scale to >= 2^-126.
+ * Arithmetic is fp32 (norm in fp64); the result is bitwise deterministic.
+ * Tensors of one call must not overlap, except that tensor_scale may be any
+ * read-only array. */
+#define FQ_MAX_SCALE_PARAMS 16
+typedef enum {
+    FQ_PROJ_POSITIVE = 0,   /* p >= 2^-126                                        */
+    FQ_PROJ_E4M3_BLOCK = 1  /* NVFP4 block scales: t 2^-9 <= p <= t 448           */
+} fq_scale_proj;
+typedef struct {
+    float* param;              /* device fp32 [count], updated in place            */
+    const float* grad;         /* device fp32 [count]                              */
+    float* exp_avg;            /* device fp32 [count], m; zero before step 1       */
+    float* exp_avg_sq;         /* device fp32 [count], v; zero before step 1       */
+    int64_t count;             /* >= 0                                             */
+    int32_t proj;              /* fq_scale_proj                                    */
+    const float* tensor_scale; /* FQ_PROJ_E4M3_BLOCK: device fp32, element i uses
+                                  tensor_scale[i / per_tensor]; else ignored       */
+    int64_t per_tensor;        /* FQ_PROJ_E4M3_BLOCK: >= 1                         */
+} fq_scale_param;
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay, max_grad_norm;
+} fq_adamw_hparams;
+/* host: the pages' values (lr 2e-4, betas 0.9 / 0.95, weight decay 0, clip 1.0)
+ * and eps 1e-8 */
+int fq_adamw_defaults(fq_adamw_hparams* h);
+/* bytes of device workspace fq_scale_adamw needs (8-byte aligned) */
+size_t fq_scale_adamw_workspace_size(const fq_scale_param* params, int32_t nparams);
+/* params: host array of nparams (1 .. FQ_MAX_SCALE_PARAMS) descriptors; h: host;
+ * step: 1 for the first step (bias corrections); grad_norm: nullable device fp32
+ * [1], receives ||g|| before clipping.  Errors: FQ_E_INVALID for null or
+ * non-finite arguments, betas outside [0, 1), eps <= 0, negative lr, weight
+ * decay or count, step < 1, a bad proj or per_tensor; FQ_E_ALIGN for pointers
+ * not 4-byte aligned (workspace: 8); FQ_E_WORKSPACE if workspace_bytes is short. */
+int fq_scale_adamw(const fq_scale_param* params, int32_t nparams, const fq_adamw_hparams* h, int64_t step,
+                   float* grad_norm, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- diagnostics ----------------------------------------------------------- */
 const char* fq_status_string(int32_t status);   /* static string                */
 const char* fq_last_hip_error(void);            /* thread-local; after FQ_E_HIP */

@@ -4,6 +4,7 @@
 // Host side only: argument validation (always before any HIP call, so every
 // error path is testable without a GPU), the layout of the saved and
 // workspace buffers, and the launch order of the forward and backward stages.
+#include <cmath>
 #include <type_traits>
 
 #include "fq.h"
@@ -742,6 +743,74 @@ int fq_grouped_expert_bwd(const fq_layer_desc* L, const fq_expert_params* P, con
         FQ_TRY(launch_tensor_bwd(ta, st));
     }
     FQ_TRY(mark(events, FQ_BWD_STAGES, st));
+    return FQ_OK;
+}
+
+int fq_adamw_defaults(fq_adamw_hparams* h) {
+    if (!h) return FQ_E_INVALID;
+    h->lr = 2.0e-4f;
+    h->beta1 = 0.9f;
+    h->beta2 = 0.95f;
+    h->eps = 1.0e-8f;
+    h->weight_decay = 0.0f;
+    h->max_grad_norm = 1.0f;
+    return FQ_OK;
+}
+
+size_t fq_scale_adamw_workspace_size(const fq_scale_param* params, int32_t nparams) {
+    int64_t nb = 0;
+    if (params && nparams > 0 && nparams <= FQ_MAX_SCALE_PARAMS)
+        for (int i = 0; i < nparams; ++i) nb += adam_norm_blocks(params[i].count > 0 ? params[i].count : 0);
+    return round_up((size_t)(nb > 0 ? nb : 1) * sizeof(double) + sizeof(double), 256);
+}
+
+int fq_scale_adamw(const fq_scale_param* params, int32_t nparams, const fq_adamw_hparams* h, int64_t step,
+                   float* grad_norm, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!params || !h || nparams < 1 || nparams > FQ_MAX_SCALE_PARAMS || step < 1) return FQ_E_INVALID;
+    const float hv[6] = {h->lr, h->beta1, h->beta2, h->eps, h->weight_decay, h->max_grad_norm};
+    for (float v : hv)
+        if (!std::isfinite(v)) return FQ_E_INVALID;
+    if (h->lr < 0 || h->beta1 < 0 || h->beta1 >= 1 || h->beta2 < 0 || h->beta2 >= 1 || h->eps <= 0 ||
+        h->weight_decay < 0)
+        return FQ_E_INVALID;
+    AdamArgs a{};
+    int64_t nb = 0;
+    for (int i = 0; i < nparams; ++i) {
+        const fq_scale_param& q = params[i];
+        if (q.count < 0 || (q.proj != FQ_PROJ_POSITIVE && q.proj != FQ_PROJ_E4M3_BLOCK)) return FQ_E_INVALID;
+        if (q.proj == FQ_PROJ_E4M3_BLOCK && (!q.tensor_scale || q.per_tensor < 1)) return FQ_E_INVALID;
+        if (q.count > 0 && (!q.param || !q.grad || !q.exp_avg || !q.exp_avg_sq)) return FQ_E_INVALID;
+        if (!aligned(q.param, 4) || !aligned(q.grad, 4) || !aligned(q.exp_avg, 4) || !aligned(q.exp_avg_sq, 4) ||
+            !aligned(q.tensor_scale, 4))
+            return FQ_E_ALIGN;
+        const int64_t per = q.per_tensor > 0 ? q.per_tensor : 1;
+        const bool vec = q.count % 4 == 0 && aligned(q.param, 16) && aligned(q.grad, 16) &&
+                         aligned(q.exp_avg, 16) && aligned(q.exp_avg_sq, 16) &&
+                         (q.proj != FQ_PROJ_E4M3_BLOCK || per % 4 == 0);
+        a.prm[i] = AdamParam{q.param, q.grad, q.exp_avg, q.exp_avg_sq, q.count, nb, q.proj, vec ? 1 : 0,
+                             q.tensor_scale, per};
+        nb += adam_norm_blocks(q.count);
+    }
+    if (grad_norm && !aligned(grad_norm, 4)) return FQ_E_ALIGN;
+    if (!workspace || !aligned(workspace, 8)) return workspace ? FQ_E_ALIGN : FQ_E_WORKSPACE;
+    if (workspace_bytes < fq_scale_adamw_workspace_size(params, nparams)) return FQ_E_WORKSPACE;
+    a.np = nparams;
+    a.nb = nb;
+    a.b1 = h->beta1;
+    a.b2 = h->beta2;
+    a.one_m_b1 = (float)(1.0 - (double)h->beta1);
+    a.one_m_b2 = (float)(1.0 - (double)h->beta2);
+    a.eps = h->eps;
+    a.decay = (float)(1.0 - (double)h->lr * (double)h->weight_decay);
+    const double bc1 = 1.0 - std::pow((double)h->beta1, (double)step);
+    const double bc2 = 1.0 - std::pow((double)h->beta2, (double)step);
+    a.step_size = (float)((double)h->lr / bc1);
+    a.bc2_sqrt = (float)std::sqrt(bc2);
+    a.max_norm = h->max_grad_norm;
+    a.part = static_cast<double*>(workspace);
+    a.clip = reinterpret_cast<float*>(static_cast<double*>(workspace) + a.nb);
+    a.norm_out = grad_norm;
+    FQ_TRY(launch_scale_adamw(a, static_cast<hipStream_t>(stream)));
     return FQ_OK;
 }
 

@@ -191,4 +191,38 @@ hipError_t launch_gemm_dgrad(const GemmArgs& g, hipStream_t st);  // B N-contigu
 hipError_t launch_gemm_wgrad(const GemmArgs& g, hipStream_t st);  // C[e] fp32 [N, K] = A_e^T B_e
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);
 
+// ------------------------------------------------------- scale optimiser ---
+// One AdamW step over up to MAX_SCALE_PARAMS fp32 tensors, gradients clipped by
+// their global L2 norm.  The host folds the bias corrections into step_size
+// and bc2_sqrt.
+constexpr int MAX_SCALE_PARAMS = 16;
+constexpr int64_t ADAM_CHUNK = 16384;   // elements per block of the norm pass
+struct AdamParam {
+    float* p;
+    const float* g;
+    float* m;
+    float* v;
+    int64_t n;                    // elements
+    int64_t blk0;                 // this tensor's first block of the norm pass
+    int32_t proj;                 // 0: >= 2^-126; 1: [t 2^-9, t 448], t = t[i / per_t]
+    int32_t vec;                  // 1: 4 elements per access (16-B aligned, n and per_t % 4 == 0)
+    const float* t;
+    int64_t per_t;
+};
+struct AdamArgs {
+    AdamParam prm[MAX_SCALE_PARAMS];
+    int32_t np;
+    int64_t nb;                   // blocks of the norm pass, over every tensor
+    float b1, b2, one_m_b1, one_m_b2, eps;
+    float decay;                  // 1 - lr wd
+    float step_size;              // lr / (1 - b1^t)
+    float bc2_sqrt;               // sqrt(1 - b2^t)
+    double max_norm;              // <= 0: no clipping
+    double* part;                 // workspace [nb]: partial sums of g^2
+    float* clip;                  // workspace [1]: the factor applied to every gradient
+    float* norm_out;              // nullable [1]: the global norm before clipping
+};
+int64_t adam_norm_blocks(int64_t count);   // norm-pass blocks of one tensor
+hipError_t launch_scale_adamw(const AdamArgs& a, hipStream_t st);
+
 }  // namespace fq

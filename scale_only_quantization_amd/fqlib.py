@@ -58,6 +58,20 @@ class ExpertGrads(Structure):
     _fields_ = [("ds_w1", c_void_p), ("ds_w2", c_void_p), ("ds_a1", c_void_p), ("ds_a2", c_void_p)]
 
 
+class ScaleParam(Structure):
+    _fields_ = [("param", c_void_p), ("grad", c_void_p), ("exp_avg", c_void_p), ("exp_avg_sq", c_void_p),
+                ("count", c_int64), ("proj", c_int32), ("tensor_scale", c_void_p), ("per_tensor", c_int64)]
+
+
+class AdamWHparams(Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("max_grad_norm", ctypes.c_float)]
+
+
+FQ_PROJ_POSITIVE, FQ_PROJ_E4M3_BLOCK = 0, 1
+FQ_MAX_SCALE_PARAMS = 16
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m scale_only_quantization_amd.build`")
@@ -90,6 +104,10 @@ def _load():
                                             c_void_p, c_void_p, c_size_t, c_void_p, c_void_p,
                                             POINTER(ExpertGrads), c_void_p, c_size_t, c_void_p,
                                             c_void_p]),
+        "fq_adamw_defaults": (c_int32, [POINTER(AdamWHparams)]),
+        "fq_scale_adamw_workspace_size": (c_size_t, [POINTER(ScaleParam), c_int32]),
+        "fq_scale_adamw": (c_int32, [POINTER(ScaleParam), c_int32, POINTER(AdamWHparams), c_int64, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -102,7 +120,8 @@ _lib = _load()
 EXPORTS = ("fq_abi_version", "fq_status_string", "fq_last_hip_error", "fq_preset",
            "fq_tensor_workspace_size", "fq_tensor", "fq_grouped_expert_saved_size",
            "fq_grouped_expert_workspace_size", "fq_grouped_expert_buffer",
-           "fq_grouped_expert_fwd", "fq_grouped_expert_bwd")
+           "fq_grouped_expert_fwd", "fq_grouped_expert_bwd", "fq_adamw_defaults",
+           "fq_scale_adamw_workspace_size", "fq_scale_adamw")
 
 
 def lib():
@@ -223,3 +242,37 @@ def bwd(L: LayerDesc, P: ExpertParams, x, topk_ids, topk_w, dy, saved, dx, d_top
                                     _ptr(d_topk_w), ctypes.byref(G), _ptr(workspace),
                                     _nbytes(workspace), _stream(stream), _events(events))
     _check(st, "fq_grouped_expert_bwd")
+
+
+# ------------------------------------------------------------ scale optimiser --
+def adamw_defaults(**over) -> AdamWHparams:
+    """The pages' optimiser settings (eps 1e-8), with keyword overrides."""
+    h = AdamWHparams()
+    _check(_lib.fq_adamw_defaults(ctypes.byref(h)), "fq_adamw_defaults")
+    for k, v in over.items():
+        setattr(h, k, v)
+    return h
+
+
+def scale_param(param, grad, exp_avg, exp_avg_sq, tensor_scale=None, per_tensor=1) -> ScaleParam:
+    """One fp32 scale tensor with its gradient and moments; with tensor_scale,
+    NVFP4 block scales projected into the E4M3 range of s / t."""
+    n = param.numel()
+    for t in (grad, exp_avg, exp_avg_sq):
+        assert t.numel() == n and t.is_contiguous()
+    proj = FQ_PROJ_POSITIVE if tensor_scale is None else FQ_PROJ_E4M3_BLOCK
+    return ScaleParam(param.data_ptr(), grad.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), n, proj,
+                      None if tensor_scale is None else tensor_scale.data_ptr(), per_tensor)
+
+
+def scale_adamw_workspace_size(params) -> int:
+    arr = (ScaleParam * len(params))(*params)
+    return _lib.fq_scale_adamw_workspace_size(arr, len(params))
+
+
+def scale_adamw(params, hp: AdamWHparams, step: int, grad_norm=None, workspace=None, stream=None):
+    """One AdamW step over `params` (a list of ScaleParam) on the stream."""
+    arr = (ScaleParam * len(params))(*params)
+    st = _lib.fq_scale_adamw(arr, len(params), ctypes.byref(hp), step, _ptr(grad_norm), _ptr(workspace),
+                             _nbytes(workspace), _stream(stream))
+    _check(st, "fq_scale_adamw")

@@ -168,3 +168,46 @@ def test_layer_validation():
     G = F.ExpertGrads(None, None, FAKE, None)
     assert lib.fq_grouped_expert_bwd(ctypes.byref(Lw), ctypes.byref(P), FAKE, FAKE, FAKE, FAKE, FAKE,
                                      1 << 40, FAKE, None, ctypes.byref(G), FAKE, 1 << 40, None, None) == F.FQ_E_INVALID
+
+
+def _sp(n=64, p=FAKE, g=FAKE, m=FAKE, v=FAKE, proj=0, t=None, per=1):
+    return F.ScaleParam(p, g, m, v, n, proj, t, per)
+
+
+def _adam(params, hp=None, step=1, norm=None, ws=FAKE, wsb=1 << 20):
+    arr = (F.ScaleParam * max(len(params), 1))(*params)
+    hp = hp or F.adamw_defaults()
+    return F.lib().fq_scale_adamw(arr, len(params), ctypes.byref(hp), step, norm, ws, wsb, None)
+
+
+def test_scale_adamw_defaults_and_workspace():
+    h = F.adamw_defaults()
+    assert (h.lr, h.beta1, h.beta2, h.weight_decay, h.max_grad_norm) == pytest.approx((2e-4, 0.9, 0.95, 0.0, 1.0))
+    assert h.eps == pytest.approx(1e-8)
+    # one double per norm block (16384 elements each, 1 .. 1024 blocks) plus the clip factor
+    small = F.scale_adamw_workspace_size([_sp(100)])
+    assert small >= 16 and small % 256 == 0
+    big = F.scale_adamw_workspace_size([_sp(25_165_824), _sp(12_582_912), _sp(128), _sp(128)])
+    assert big >= 1024 * 8 + 8
+
+
+def test_scale_adamw_validation():
+    ok = [_sp()]
+    assert F.lib().fq_scale_adamw(None, 1, ctypes.byref(F.adamw_defaults()), 1, None, FAKE, 1 << 20,
+                                  None) == F.FQ_E_INVALID
+    assert _adam([]) == F.FQ_E_INVALID                                     # no tensor
+    assert _adam([_sp()] * 17) == F.FQ_E_INVALID                           # more than 16
+    assert _adam(ok, step=0) == F.FQ_E_INVALID
+    for bad in (dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(lr=-1.0), dict(weight_decay=-1.0),
+                dict(lr=float("nan")), dict(max_grad_norm=float("inf"))):
+        assert _adam(ok, hp=F.adamw_defaults(**bad)) == F.FQ_E_INVALID, bad
+    assert _adam([_sp(n=-1)]) == F.FQ_E_INVALID
+    assert _adam([_sp(g=None)]) == F.FQ_E_INVALID
+    assert _adam([_sp(proj=2)]) == F.FQ_E_INVALID
+    assert _adam([_sp(proj=1)]) == F.FQ_E_INVALID                          # block projection needs t
+    assert _adam([_sp(proj=1, t=FAKE, per=0)]) == F.FQ_E_INVALID
+    assert _adam([_sp(m=MIS)]) == F.FQ_E_ALIGN
+    assert _adam(ok, norm=MIS) == F.FQ_E_ALIGN
+    assert _adam(ok, ws=None) == F.FQ_E_WORKSPACE
+    assert _adam(ok, ws=FAKE + 4) == F.FQ_E_ALIGN
+    assert _adam(ok, wsb=8) == F.FQ_E_WORKSPACE
