@@ -23,6 +23,8 @@ layer     the SwiGLU expert layer forward and backward (float64 GEMMs).
 presets   the six format names mapped to four quantiser descriptors.
 optim     the scale optimiser step: AdamW with global-norm clipping and the
           range projection of the updated scales.
+distill   the self-distillation losses on logits (kl, rkl, cakld, top-k kl) with
+          the LM cross entropy, and their gradients.
 
 Precision: every codec step is IEEE float32 (numpy float32 arithmetic is
 correctly rounded); GEMMs, gradients and sums are float64.  Pure-Python loops
