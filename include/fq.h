@@ -323,6 +323,54 @@ size_t fq_scale_adamw_workspace_size(const fq_scale_param* params, int32_t npara
 int fq_scale_adamw(const fq_scale_param* params, int32_t nparams, const fq_adamw_hparams* h, int64_t step,
                    float* grad_norm, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- distillation losses ---------------------------------------------------
+ * The loss of quantisation-aware distillation on one batch of logits, and its
+ * gradient on the student's logits (the nxmr.cn article, section 二.5:
+ * total = lm_weight * lm_loss + distill_weight * distill_loss, distill_type kl,
+ * rkl or cakld, and with distill_topk > 0 the KL only over the teacher's
+ * top-k tokens so that the [tokens, vocab] teacher tensor never exists; the
+ * AngelSlim page, "Train from YAML").  The teacher is the same frozen model
+ * with its quantisers disabled (FQ_NONE descriptors in this library).
+ * Readings (the pages give no formulas): temperature 1; every term is the
+ * mean over tokens; lm_loss is the cross entropy of the student at the label;
+ * with p the teacher's and q the student's softmax:
+ *     kl = KL(p || q), rkl = KL(q || p),
+ *     cakld = c kl + (1 - c) rkl, c = max_v p (the teacher's confidence);
+ *     top-k kl = sum over the k given ids of p~ (log p~ - log q), p~ the softmax
+ *     of the teacher's k logits, log q the student's full log-softmax there.
+ * Arithmetic fp32, reductions in a fixed order: bitwise deterministic. */
+typedef enum {
+    FQ_DISTILL_KL = 0,
+    FQ_DISTILL_RKL = 1,
+    FQ_DISTILL_CAKLD = 2,
+    FQ_DISTILL_TOPK_KL = 3
+} fq_distill_type;
+typedef struct {
+    int32_t type;              /* fq_distill_type                                     */
+    int32_t topk;              /* FQ_DISTILL_TOPK_KL: k in [1, 64]; else 0            */
+    float lm_weight;           /* weight of the LM cross entropy (needs labels)       */
+    float distill_weight;      /* weight of the distillation term                     */
+} fq_distill_desc;
+/* bytes of device workspace: one fp32 per token (row losses) unless the caller
+ * passes row_loss */
+size_t fq_distill_workspace_size(int64_t tokens);
+/* student_logits: device bf16 [tokens, vocab], vocab % 8 == 0, 16-B aligned.
+ * teacher_logits: device bf16 [tokens, vocab] for kl / rkl / cakld, else NULL.
+ * teacher_topk_logits / teacher_topk_ids: device fp32 / int32 [tokens, topk]
+ *   for the top-k kl (ids distinct and in [0, vocab)), else NULL.
+ * labels: nullable device int32 [tokens] in [0, vocab): adds the LM term.
+ * loss: device fp32 [1], the mean total loss.  row_loss: nullable device fp32
+ *   [tokens], each token's total loss.  grad: nullable device bf16
+ *   [tokens, vocab], d loss / d student_logits (16-B aligned).
+ * With tokens == 0 the logits may be NULL and loss receives 0.
+ * Errors: FQ_E_INVALID (nulls, bad type or topk, non-finite weights),
+ * FQ_E_SHAPE (tokens < 0, vocab < 8 or not a multiple of 8, vocab >= 2^31),
+ * FQ_E_ALIGN, FQ_E_WORKSPACE. */
+int fq_distill_loss(const fq_distill_desc* d, int64_t tokens, int64_t vocab, const void* student_logits,
+                    const void* teacher_logits, const float* teacher_topk_logits,
+                    const int32_t* teacher_topk_ids, const int32_t* labels, float* loss, float* row_loss,
+                    void* grad, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- diagnostics ----------------------------------------------------------- */
 const char* fq_status_string(int32_t status);   /* static string                */
 const char* fq_last_hip_error(void);            /* thread-local; after FQ_E_HIP */

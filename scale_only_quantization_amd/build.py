@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfq.so")
-SOURCES = ["fq_api.hip", "fq_tensor.hip", "fq_layer.hip", "fq_gemm.hip", "fq_optim.hip"]
+SOURCES = ["fq_api.hip", "fq_tensor.hip", "fq_layer.hip", "fq_gemm.hip", "fq_optim.hip", "fq_distill.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

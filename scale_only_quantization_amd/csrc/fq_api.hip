@@ -814,4 +814,52 @@ int fq_scale_adamw(const fq_scale_param* params, int32_t nparams, const fq_adamw
     return FQ_OK;
 }
 
+size_t fq_distill_workspace_size(int64_t tokens) {
+    return round_up((size_t)(tokens > 0 ? tokens : 1) * sizeof(float), 256);
+}
+
+int fq_distill_loss(const fq_distill_desc* d, int64_t tokens, int64_t vocab, const void* student_logits,
+                    const void* teacher_logits, const float* teacher_topk_logits,
+                    const int32_t* teacher_topk_ids, const int32_t* labels, float* loss, float* row_loss,
+                    void* grad, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!d || !loss || (tokens > 0 && !student_logits)) return FQ_E_INVALID;   // no tokens: nothing is read
+    if (d->type < FQ_DISTILL_KL || d->type > FQ_DISTILL_TOPK_KL) return FQ_E_INVALID;
+    if (!std::isfinite(d->lm_weight) || !std::isfinite(d->distill_weight)) return FQ_E_INVALID;
+    if (tokens < 0 || vocab < 8 || vocab % 8 || vocab >= ((int64_t)1 << 31)) return FQ_E_SHAPE;
+    const bool topk = d->type == FQ_DISTILL_TOPK_KL;
+    if (topk) {
+        if (d->topk < 1 || d->topk > 64 || d->topk > vocab ||
+            (tokens > 0 && (!teacher_topk_logits || !teacher_topk_ids)))
+            return FQ_E_INVALID;
+    } else if (d->topk != 0 || (tokens > 0 && !teacher_logits)) {
+        return FQ_E_INVALID;
+    }
+    if (!aligned(student_logits, 16) || (!topk && !aligned(teacher_logits, 16)) || (grad && !aligned(grad, 16)) ||
+        !aligned(loss, 4) || (row_loss && !aligned(row_loss, 4)) || (labels && !aligned(labels, 4)) ||
+        (topk && (!aligned(teacher_topk_logits, 4) || !aligned(teacher_topk_ids, 4))))
+        return FQ_E_ALIGN;
+    if (!row_loss) {
+        if (!workspace) return FQ_E_WORKSPACE;
+        if (!aligned(workspace, 4)) return FQ_E_ALIGN;
+        if (workspace_bytes < fq_distill_workspace_size(tokens)) return FQ_E_WORKSPACE;
+    }
+    DistillArgs a{};
+    a.kind = d->type;
+    a.T = tokens;
+    a.V = vocab;
+    a.zs = static_cast<const uint16_t*>(student_logits);
+    a.zt = topk ? nullptr : static_cast<const uint16_t*>(teacher_logits);
+    a.top_v = topk ? teacher_topk_logits : nullptr;
+    a.top_i = topk ? teacher_topk_ids : nullptr;
+    a.k = topk ? d->topk : 0;
+    a.labels = labels;
+    a.lm_w = d->lm_weight;
+    a.dist_w = d->distill_weight;
+    a.inv_T = tokens > 0 ? (float)(1.0 / (double)tokens) : 0.0f;
+    a.row_loss = row_loss ? row_loss : static_cast<float*>(workspace);
+    a.grad = static_cast<uint16_t*>(grad);
+    FQ_TRY(launch_distill(a, loss, static_cast<hipStream_t>(stream)));
+    return FQ_OK;
+}
+
 }  // extern "C"

@@ -225,4 +225,22 @@ struct AdamArgs {
 int64_t adam_norm_blocks(int64_t count);   // norm-pass blocks of one tensor
 hipError_t launch_scale_adamw(const AdamArgs& a, hipStream_t st);
 
+// ------------------------------------------------- distillation losses ---
+enum DistillKind : int { DK_KL = 0, DK_RKL = 1, DK_CAKLD = 2, DK_TOPK = 3 };
+struct DistillArgs {
+    int kind;
+    int64_t T, V;                 // rows (tokens), vocabulary (multiple of 8)
+    const uint16_t* zs;           // bf16 [T, V] student logits
+    const uint16_t* zt;           // bf16 [T, V] teacher logits (kl, rkl, cakld)
+    const float* top_v;           // fp32 [T, k] the teacher's top-k logits (top-k kl)
+    const int32_t* top_i;         // [T, k] their token ids
+    int k;
+    const int32_t* labels;        // nullable [T]: the LM term
+    float lm_w, dist_w, inv_T;
+    float* row_loss;              // [T]
+    uint16_t* grad;               // nullable bf16 [T, V]
+};
+// the row losses, their mean into mean_out[0] and, with a.grad, d mean / d zs
+hipError_t launch_distill(const DistillArgs& a, float* mean_out, hipStream_t st);
+
 }  // namespace fq

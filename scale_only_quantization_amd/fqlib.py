@@ -68,6 +68,12 @@ class AdamWHparams(Structure):
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("max_grad_norm", ctypes.c_float)]
 
 
+class DistillDesc(Structure):
+    _fields_ = [("type", c_int32), ("topk", c_int32), ("lm_weight", ctypes.c_float),
+                ("distill_weight", ctypes.c_float)]
+
+
+DISTILL_TYPES = {"kl": 0, "rkl": 1, "cakld": 2, "topk_kl": 3}
 FQ_PROJ_POSITIVE, FQ_PROJ_E4M3_BLOCK = 0, 1
 FQ_MAX_SCALE_PARAMS = 16
 
@@ -108,6 +114,10 @@ def _load():
         "fq_scale_adamw_workspace_size": (c_size_t, [POINTER(ScaleParam), c_int32]),
         "fq_scale_adamw": (c_int32, [POINTER(ScaleParam), c_int32, POINTER(AdamWHparams), c_int64, c_void_p,
                                      c_void_p, c_size_t, c_void_p]),
+        "fq_distill_workspace_size": (c_size_t, [c_int64]),
+        "fq_distill_loss": (c_int32, [POINTER(DistillDesc), c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                      c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -121,7 +131,7 @@ EXPORTS = ("fq_abi_version", "fq_status_string", "fq_last_hip_error", "fq_preset
            "fq_tensor_workspace_size", "fq_tensor", "fq_grouped_expert_saved_size",
            "fq_grouped_expert_workspace_size", "fq_grouped_expert_buffer",
            "fq_grouped_expert_fwd", "fq_grouped_expert_bwd", "fq_adamw_defaults",
-           "fq_scale_adamw_workspace_size", "fq_scale_adamw")
+           "fq_scale_adamw_workspace_size", "fq_scale_adamw", "fq_distill_workspace_size", "fq_distill_loss")
 
 
 def lib():
@@ -276,3 +286,19 @@ def scale_adamw(params, hp: AdamWHparams, step: int, grad_norm=None, workspace=N
     st = _lib.fq_scale_adamw(arr, len(params), ctypes.byref(hp), step, _ptr(grad_norm), _ptr(workspace),
                              _nbytes(workspace), _stream(stream))
     _check(st, "fq_scale_adamw")
+
+
+# --------------------------------------------------------- distillation loss --
+def distill_desc(kind: str, topk: int = 0, lm_weight: float = 1.0, distill_weight: float = 1.0) -> DistillDesc:
+    return DistillDesc(DISTILL_TYPES[kind], topk, lm_weight, distill_weight)
+
+
+def distill_loss(d: DistillDesc, student, loss, teacher=None, top_v=None, top_i=None, labels=None,
+                 row_loss=None, grad=None, workspace=None, stream=None):
+    """Loss (mean into loss[0]) and, with grad, d loss / d student for student
+    logits [tokens, vocab] (bf16)."""
+    T, V = student.shape
+    st = _lib.fq_distill_loss(ctypes.byref(d), T, V, _ptr(student), _ptr(teacher), _ptr(top_v), _ptr(top_i),
+                              _ptr(labels), _ptr(loss), _ptr(row_loss), _ptr(grad), _ptr(workspace),
+                              _nbytes(workspace), _stream(stream))
+    _check(st, "fq_distill_loss")

@@ -211,3 +211,30 @@ def test_scale_adamw_validation():
     assert _adam(ok, ws=None) == F.FQ_E_WORKSPACE
     assert _adam(ok, ws=FAKE + 4) == F.FQ_E_ALIGN
     assert _adam(ok, wsb=8) == F.FQ_E_WORKSPACE
+
+
+def _dl(d, T=4, V=64, zs=FAKE, zt=FAKE, tv=None, ti=None, lab=None, loss=FAKE, rows=None, grad=None,
+        ws=FAKE, wsb=1 << 16):
+    return F.lib().fq_distill_loss(ctypes.byref(d), T, V, zs, zt, tv, ti, lab, loss, rows, grad, ws, wsb, None)
+
+
+def test_distill_validation():
+    kl = F.distill_desc("kl")
+    assert F.lib().fq_distill_workspace_size(1000) >= 4000
+    assert _dl(F.distill_desc("kl"), zs=None) == F.FQ_E_INVALID
+    assert _dl(kl, loss=None) == F.FQ_E_INVALID
+    assert _dl(kl, zt=None) == F.FQ_E_INVALID                              # kl needs the teacher
+    assert _dl(F.DistillDesc(7, 0, 1.0, 1.0)) == F.FQ_E_INVALID
+    assert _dl(F.distill_desc("kl", topk=4)) == F.FQ_E_INVALID             # top-k only with topk_kl
+    assert _dl(F.distill_desc("kl", lm_weight=float("nan"))) == F.FQ_E_INVALID
+    tk = F.distill_desc("topk_kl", topk=8)
+    assert _dl(tk, zt=None) == F.FQ_E_INVALID                              # needs the top-k arrays
+    assert _dl(F.distill_desc("topk_kl", topk=65), tv=FAKE, ti=FAKE) == F.FQ_E_INVALID
+    assert _dl(F.distill_desc("topk_kl", topk=0), tv=FAKE, ti=FAKE) == F.FQ_E_INVALID
+    assert _dl(kl, V=60) == F.FQ_E_SHAPE
+    assert _dl(kl, V=0) == F.FQ_E_SHAPE
+    assert _dl(kl, T=-1) == F.FQ_E_SHAPE
+    assert _dl(kl, zs=MIS) == F.FQ_E_ALIGN
+    assert _dl(kl, grad=FAKE + 8) == F.FQ_E_ALIGN
+    assert _dl(kl, ws=None) == F.FQ_E_WORKSPACE
+    assert _dl(kl, wsb=8) == F.FQ_E_WORKSPACE
