@@ -197,6 +197,49 @@ def scale_adamw_step(ev, F, dl, L, reps=20, warmup=3):
                 elements=count, tensors=len(params))
 
 
+def distill_logits(ev, F, T=16384, V=151936, k=64, reps=5, warmup=2):
+    """The distillation loss and its gradient on one batch of logits shaped like
+    the pages' Qwen3 runs (seq 2048 x micro-batch 8 tokens, the Qwen3
+    vocabulary), student and teacher bf16, seeded on the device.  Algorithmic
+    bytes: each logit read once and the bf16 gradient written once (6 B per
+    element with the full teacher, 4 B with its top-k)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2024)
+    zs = (torch.randn((T, V), generator=g, device="cuda") * 2.0).to(torch.bfloat16)
+    zt = (zs.float() * 1.3 + torch.randn((T, V), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    labels = torch.randint(0, V, (T,), generator=g, device="cuda", dtype=torch.int32)
+    tv, ti = torch.topk(zt.float(), k, dim=-1)
+    ti = ti.to(torch.int32).contiguous()
+    grad = torch.empty_like(zs)
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(F.lib().fq_distill_workspace_size(T) // 4, dtype=torch.float32, device="cuda")
+    out = {}
+    for kind, kk, kw, per in (("cakld", 0, dict(teacher=zt), 6), ("topk_kl", k, dict(top_v=tv, top_i=ti), 4)):
+        d = F.distill_desc(kind, topk=kk)
+
+        def fn():
+            F.distill_loss(d, zs, loss, labels=labels, grad=grad, workspace=ws, **kw)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev.create(2)
+        ev.record(e0)
+        for _ in range(reps):
+            fn()
+        ev.record(e1)
+        ev.sync(e1)
+        ms = ev.elapsed_ms(e0, e1) / reps
+        alg = per * T * V
+        gbs = alg / (ms * 1e-3) / 1e9
+        out[kind] = dict(ms=round(ms, 4), gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 3), bytes=alg)
+    out["shape"] = [T, V]
+    out["topk"] = k
+    del zs, zt, grad, tv, ti
+    torch.cuda.empty_cache()
+    return out
+
+
 def fake_quant_stack(ev, F, reps=20, warmup=3):
     """Standalone fq_tensor on the weight-only microbench stack: 128 expert
     matrices 768 x 2048 bf16 N(0, 0.02) with 0.1% outliers x 20, NVFP4 block-16
@@ -409,6 +452,10 @@ def main():
     out["fake_quant"] = fake_quant_stack(ev, F)
     if args.stages:
         print(f"[bench] fake_quant {out['fake_quant']}", file=sys.stderr)
+    print("[bench] distillation loss on a Qwen3-sized batch of logits ...", file=sys.stderr, flush=True)
+    out["distill"] = distill_logits(ev, F)
+    if args.stages:
+        print(f"[bench] distill {out['distill']}", file=sys.stderr)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a bounded sample ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(data, P, fmt)

@@ -89,28 +89,37 @@ __global__ __launch_bounds__(DTPB) void k_distill(DistillArgs a) {
             float mv = fs[0];
 #pragma unroll
             for (int i = 1; i < 8; ++i) mv = fmaxf(mv, fs[i]);
+            // running sums rescaled only when the vector raises the running max
             if (KIND != DK_TOPK) {
                 unpack8(zt[v], ft);
                 float mt = ft[0];
 #pragma unroll
                 for (int i = 1; i < 8; ++i) mt = fmaxf(mt, ft[i]);
-                float s2 = 0.0f, a2 = 0.0f;
+                if (mt > st_.m) {
+                    const float f = __expf(st_.m - mt);
+                    st_.s *= f;
+                    st_.a *= f;
+                    st_.m = mt;
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float e = __expf(ft[i] - mt);
-                    s2 += e;
-                    a2 += e * (ft[i] - fs[i]);
+                    const float e = __expf(ft[i] - st_.m);
+                    st_.s += e;
+                    st_.a += e * (ft[i] - fs[i]);
                 }
-                st_.merge(mt, s2, a2);
             }
-            float s2 = 0.0f, b2 = 0.0f;
+            if (mv > ss_.m) {
+                const float f = __expf(ss_.m - mv);
+                ss_.s *= f;
+                ss_.a *= f;
+                ss_.m = mv;
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float e = __expf(fs[i] - mv);
-                s2 += e;
-                if (KIND == DK_RKL || KIND == DK_CAKLD) b2 += e * (fs[i] - ft[i]);
+                const float e = __expf(fs[i] - ss_.m);
+                ss_.s += e;
+                if (KIND == DK_RKL || KIND == DK_CAKLD) ss_.a += e * (fs[i] - ft[i]);
             }
-            ss_.merge(mv, s2, b2);
         }
         block_merge(st_, ss_, red);
         const float lse_s = ss_.m + __logf(ss_.s);
@@ -221,7 +230,7 @@ hipError_t launch_distill(const DistillArgs& a, float* mean_out, hipStream_t st)
         hipError_t err = hipGetDevice(&dev);
         if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
-        const int64_t grid = a.T < (int64_t)cus * 4 ? a.T : (int64_t)cus * 4;
+        const int64_t grid = a.T < (int64_t)cus * 2 ? a.T : (int64_t)cus * 2;   // two rows in flight per CU (measured best of 1, 2, 4)
         switch (a.kind) {
         case DK_KL: hipLaunchKernelGGL(k_distill<DK_KL>, dim3((unsigned)grid), dim3(DTPB), 0, st, a); break;
         case DK_RKL: hipLaunchKernelGGL(k_distill<DK_RKL>, dim3((unsigned)grid), dim3(DTPB), 0, st, a); break;
