@@ -196,7 +196,7 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);
 // their global L2 norm.  The host folds the bias corrections into step_size
 // and bc2_sqrt.
 constexpr int MAX_SCALE_PARAMS = 16;
-constexpr int64_t ADAM_CHUNK = 16384;   // elements per block of the norm pass
+constexpr int64_t ADAM_CHUNK = 32768;   // elements per block of the norm pass
 struct AdamParam {
     float* p;
     const float* g;

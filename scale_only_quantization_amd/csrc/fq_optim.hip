@@ -27,14 +27,17 @@ namespace {
 
 constexpr int OPT_TPB = 256;
 
+// fixed order: a wave xor-tree, then the waves' sums in wave order
 __device__ __forceinline__ double block_sum(double v, double* red) {
-    red[threadIdx.x] = v;
+#pragma unroll
+    for (int m = 1; m < WAVE; m <<= 1) v += __shfl_xor(v, m);
+    if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = v;
     __syncthreads();
-    for (int w = OPT_TPB / 2; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
-    }
-    return red[0];
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < OPT_TPB / WAVE; ++w) t += red[w];
+    __syncthreads();
+    return t;
 }
 
 __global__ __launch_bounds__(OPT_TPB) void k_adam_sq(AdamArgs a) {
@@ -46,8 +49,19 @@ __global__ __launch_bounds__(OPT_TPB) void k_adam_sq(AdamArgs a) {
     const int64_t hi = min(lo + ADAM_CHUNK, q.n);
     double acc = 0.0;
     if (q.vec) {
+        // four independent 16-B loads in flight per thread, summed in order
         const float4* g4 = reinterpret_cast<const float4*>(q.g);
-        for (int64_t k = lo / 4 + threadIdx.x; k < hi / 4; k += OPT_TPB) {
+        int64_t k = lo / 4 + threadIdx.x;
+        for (; k + 3 * OPT_TPB < hi / 4; k += 4 * OPT_TPB) {
+            float4 g[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) g[u] = g4[k + u * OPT_TPB];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                acc += (double)g[u].x * g[u].x + (double)g[u].y * g[u].y + (double)g[u].z * g[u].z +
+                       (double)g[u].w * g[u].w;
+        }
+        for (; k < hi / 4; k += OPT_TPB) {
             const float4 g = g4[k];
             acc += (double)g.x * g.x + (double)g.y * g.y + (double)g.z * g.z + (double)g.w * g.w;
         }
