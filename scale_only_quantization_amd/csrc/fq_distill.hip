@@ -1,7 +1,8 @@
 // Self-distillation losses on logits (the nxmr.cn article, section 二.5:
 // total = lm_weight lm_loss + distill_weight distill_loss; distill_type kl,
 // rkl or cakld; distill_topk > 0 restricts the KL to the teacher's top-k
-// tokens).  One block per token row, two passes over the row, no atomics:
+// tokens).  One 1024-thread block per token row, two passes over the row, no
+// atomics:
 //   pass 1  online (max, sum of exp) of the student's and the teacher's
 //           logits, with the sums the losses need:
 //             A = sum e^{zt - mt} (zt - zs)   -> kl  = A / St + lse_s - lse_t
@@ -24,7 +25,7 @@
 namespace fq {
 namespace {
 
-constexpr int DTPB = 512;
+constexpr int DTPB = 1024;
 constexpr int DWAVES = DTPB / WAVE;
 
 // a token id from the caller, kept inside the row (ids are a precondition)
@@ -230,7 +231,9 @@ hipError_t launch_distill(const DistillArgs& a, float* mean_out, hipStream_t st)
         hipError_t err = hipGetDevice(&dev);
         if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
-        const int64_t grid = a.T < (int64_t)cus * 2 ? a.T : (int64_t)cus * 2;   // two rows in flight per CU (measured best of 1, 2, 4)
+        // one row in flight per CU: the rows in flight (256 x 608 KB at the Qwen3
+        // vocabulary) then fit the last-level cache, and pass 2 re-reads from it
+        const int64_t grid = a.T < (int64_t)cus ? a.T : (int64_t)cus;
         switch (a.kind) {
         case DK_KL: hipLaunchKernelGGL(k_distill<DK_KL>, dim3((unsigned)grid), dim3(DTPB), 0, st, a); break;
         case DK_RKL: hipLaunchKernelGGL(k_distill<DK_RKL>, dim3((unsigned)grid), dim3(DTPB), 0, st, a); break;
