@@ -33,17 +33,23 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 WORKLOADS = {
-    # name: (synth case, format, description)
+    # name: (synth case, format, description, backward to dX and d topk_w)
     "qwen3": ("qwen3", "nvfp4", "Qwen3-30B-A3B-shaped MoE layer nvfp4 W4A4, E=128 H=2048 I=768 top-8, "
-                                 "T=16384, Zipf(1.1) load"),
-    "qwen3_w8a8": ("qwen3u", "w8a8", "same layer w8a8, T=16384, uniform routing"),
-    "qwen3_w4afp8": ("qwen3l", "w4afp8", "same layer w4afp8, T=32768, Zipf(1.1) load"),
-    "qwen3_fp8": ("qwen3l", "fp8", "same layer fp8, T=32768, Zipf(1.1) load"),
+                                 "T=16384, Zipf(1.1) load", True),
+    # forward + weight-scale gradients only: no dX, so no fc1 data gradient or
+    # A1 backward (the A1 quantiser is dynamic and has no parameter)
+    "qwen3_w8a8": ("qwen3u", "w8a8", "same layer w8a8, T=16384, uniform routing, fwd + weight-scale grads",
+                   False),
+    "qwen3_w4afp8": ("qwen3l", "w4afp8", "same layer w4afp8, T=32768, Zipf(1.1) load", True),
+    "qwen3_fp8": ("qwen3l", "fp8", "same layer fp8, T=32768, Zipf(1.1) load", True),
 }
+# stages that do no work when the backward stops at the weight-scale gradients
+DX_STAGES = ("fc1_dgrad", "unpermute_a1", "a1_sum")
 
 
-def stage_work(L, fmt):
-    """Algorithmic bytes (HBM kernels) or FLOPs (GEMMs) of each stage per launch."""
+def stage_work(L, fmt, full_bwd=True):
+    """Algorithmic bytes (HBM kernels) or FLOPs (GEMMs) of each stage per launch;
+    without the full backward, permute_dy forms no d topk_w (no read of Y_r)."""
     E, H, I, T, k = L.E, L.H, L.I, L.T, L.k
     R = T * k
     bf, f4 = 2, 4
@@ -62,7 +68,7 @@ def stage_work(L, fmt):
         "combine": ("hbm", R * H * bf + T * H * bf + R * 4),
     }
     bwd = {
-        "permute_dy": ("hbm", T * H * bf + R * H * bf + R * H * bf),
+        "permute_dy": ("hbm", T * H * bf + R * H * bf + (R * H * bf if full_bwd else 0)),
         "fc2_dgrad": ("mfma", 2.0 * R * H * I),
         "fc2_wgrad": ("mfma", 2.0 * R * H * I),
         "swiglu_bwd": ("hbm", 2 * R * 2 * I * bf + R * I * bf),
@@ -356,7 +362,7 @@ def main():
     from tests.layer_run import DeviceLayer, spec_for
     from scale_only_quantization_amd import fqlib as F
 
-    case_name, fmt, desc = WORKLOADS[args.workload]
+    case_name, fmt, desc, full_bwd = WORKLOADS[args.workload]
     case = synth.CASES[case_name]
     t_gen = time.perf_counter()
     data = synth.make_layer(case)
@@ -373,7 +379,8 @@ def main():
     def step(i=None):
         F.fwd(dl.desc, dl.P, dl.d["X"], dl.d["ids"], dl.d["w"], dl.y, dl.saved, dl.ws,
               events=None if i is None else evf[i])
-        F.bwd(dl.desc, dl.P, dl.d["X"], dl.d["ids"], dl.d["w"], dl.d["dY"], dl.saved, dl.dx, dl.dw,
+        F.bwd(dl.desc, dl.P, dl.d["X"], dl.d["ids"], dl.d["w"], dl.d["dY"], dl.saved,
+              dl.dx if full_bwd else None, dl.dw if full_bwd else None,
               dl.G, dl.ws, events=None if i is None else evb[i])
 
     for _ in range(args.warmup):
@@ -393,8 +400,11 @@ def main():
     for pass_, stages, evs in (("fwd", F.FWD_STAGES, evf), ("bwd", F.BWD_STAGES, evb)):
         for si, n in enumerate(stages):
             dur[n] = float(np.mean([ev.elapsed_ms(e[si], e[si + 1]) for e in evs]))
-    work_f, work_b = stage_work(L, fmt)
+    work_f, work_b = stage_work(L, fmt, full_bwd)
     work = {**work_f, **work_b}
+    if not full_bwd:
+        for n in DX_STAGES:
+            dur.pop(n)
     stages = {}
     for n, d in dur.items():
         kind, amount = work[n]
@@ -405,9 +415,9 @@ def main():
             ach = amount / (d * 1e-3) / 1e9
             stages[n] = dict(ms=round(d, 4), gbs=round(ach, 1), frac=round(ach / HBM_PEAK_GBS, 3))
     # the dominant kernel: the one with the most time per step over its launches
-    per_kernel = {kn: sum(dur[n] for n in st) for kn, (st, _) in KERNELS.items()}
+    per_kernel = {kn: sum(dur[n] for n in st if n in dur) for kn, (st, _) in KERNELS.items()}
     dom = max(per_kernel, key=per_kernel.get)
-    launches = KERNELS[dom][0]
+    launches = tuple(n for n in KERNELS[dom][0] if n in dur)
     kind = work[launches[0]][0]
     amount = sum(work[n][1] for n in launches) / len(launches)      # per launch
     avg_ms = per_kernel[dom] / len(launches)
@@ -423,7 +433,7 @@ def main():
                 work_per_launch=amount)
     if args.stages:
         for n in F.FWD_STAGES + F.BWD_STAGES:
-            print(f"[bench] {n:14s} {stages[n]}", file=sys.stderr)
+            print(f"[bench] {n:14s} {stages.get(n, 'not run')}", file=sys.stderr)
 
     out = {
         "metric": "expert-layer fwd+bwd tokens/s",
@@ -439,7 +449,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "format": fmt, "experts": case.E, "hidden": case.H,
-                   "intermediate": case.I, "tokens": case.T, "topk": case.k, "routing": case.routing},
+                   "intermediate": case.I, "tokens": case.T, "topk": case.k, "routing": case.routing,
+                   "backward": "full: dX, d topk_w and every scale gradient" if full_bwd
+                   else "weight-scale gradients only"},
         "roofline": roof,
         "stages": stages,
     }

@@ -710,13 +710,22 @@ hipError_t launch(const GemmArgs& g, hipStream_t st) {
 }
 
 // out[o] = sum of `per` consecutive partials (fixed order), o < n_out
+// out[o] = sum of part[o * per .. o * per + per): L = pow2 >= per (<= 64)
+// lanes per output read its partials coalesced, lane j taking j, j + L, ...,
+// then a fixed xor tree over the L lanes (deterministic)
 __global__ __launch_bounds__(256) void k_sg_sum(const float* part, int64_t n_out, int per, float* out) {
-    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (o >= n_out) return;
-    const float* p = part + o * per;
+    int L = 1;
+    while (L < per && L < 64) L <<= 1;
+    const int lane = threadIdx.x & 63;
+    const int64_t o = ((int64_t)blockIdx.x * 256 + threadIdx.x) / L;
+    const int j0 = lane & (L - 1);
     float acc = 0.0f;
-    for (int i = 0; i < per; ++i) acc += p[i];
-    out[o] = acc;
+    if (o < n_out) {
+        const float* p = part + o * per;
+        for (int i = j0; i < per; i += L) acc += p[i];
+    }
+    acc = group_sum(acc, L);
+    if (o < n_out && j0 == 0) out[o] = acc;
 }
 
 // out[b] = sum over rows of in[b, :] (per-matrix gradient), fixed order
@@ -745,6 +754,13 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st) {
     return hipGetLastError();
 }
 
+// blocks of k_sg_sum for n_out outputs of `per` partials each
+static unsigned sg_sum_blocks(int64_t n_out, int per) {
+    int64_t L = 1;
+    while (L < per && L < 64) L <<= 1;
+    return (unsigned)((n_out * L + 255) / 256);
+}
+
 int sg_mode(const QParams& q) {
     if (q.kind == K_NONE || q.source == S_DYNAMIC) return 0;
     if (q.kind == K_NVFP4) return 1;
@@ -757,13 +773,13 @@ hipError_t launch_sg_reduce(const QParams& q, const float* part, int64_t E, int6
     const int64_t rows = E * N, np = K / 32;
     if (q.gran == G_GROUP) {
         const int64_t n_out = rows * (K / q.group);
-        hipLaunchKernelGGL(k_sg_sum, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, st, part, n_out,
+        hipLaunchKernelGGL(k_sg_sum, dim3(sg_sum_blocks(n_out, q.group / 32)), dim3(256), 0, st, part, n_out,
                            q.group / 32, out);
     } else if (q.gran == G_ROW) {
-        hipLaunchKernelGGL(k_sg_sum, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, part, rows,
+        hipLaunchKernelGGL(k_sg_sum, dim3(sg_sum_blocks(rows, (int)np)), dim3(256), 0, st, part, rows,
                            (int)np, out);
     } else {
-        hipLaunchKernelGGL(k_sg_sum, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, part, rows,
+        hipLaunchKernelGGL(k_sg_sum, dim3(sg_sum_blocks(rows, (int)np)), dim3(256), 0, st, part, rows,
                            (int)np, rowpart);
         hipLaunchKernelGGL(k_sg_batch, dim3((unsigned)E), dim3(256), 0, st, rowpart, N, out);
     }

@@ -34,6 +34,9 @@ CASES = [
     # more matrices than one launch grid dimension holds (65535): the row-per-wave path
     ("nvfp4_w_many", OP.NVFP4_W, (70000, 1, 32)),
     ("int4_g128_many", OP.INT4_G128, (66000, 1, 128)),
+    ("fp8_row_many", OP.FP8_ROW, (66000, 2, 64)),
+    # a W2-shaped per-channel stack slice: rows of 768 (96 vectors)
+    ("int8_row_768", OP.INT8_ROW, (4, 6, 768)),
 ]
 
 
