@@ -95,9 +95,13 @@ __device__ __forceinline__ float e2m1_round(float a) {
     const float c = __uint_as_float((uint32_t)(min(max(e, 1), 3) + 148) << 23);   // 2^(21 + e)
     return (a + c) - c;
 }
-// 3-bit magnitude code of an E2M1 grid value
+// 3-bit magnitude code of an E2M1 grid value: from 1 up, exponent and top
+// mantissa bit of the fp32 pattern; below 1 (0 or 0.5), 2 qm read off the low
+// bits of 2 qm + 2^23.  Both formed, one selected: no divergent branch.
 __device__ __forceinline__ uint32_t e2m1_code(float qm) {
-    return qm >= 1.0f ? (__float_as_uint(qm) >> 22) - 252u : (uint32_t)(qm * 2.0f);
+    const uint32_t hi = (__float_as_uint(qm) >> 22) - 252u;
+    const uint32_t lo = __float_as_uint(qm * 2.0f + 8388608.0f) & 1u;
+    return qm >= 1.0f ? hi : lo;
 }
 
 // --------------------------------------------------------------- division ---

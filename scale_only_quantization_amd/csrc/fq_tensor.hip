@@ -28,7 +28,7 @@ __device__ __forceinline__ float amax8(const float* f) {
 
 // Effective scale of the 8 elements of vector v of row `grow`, and the NVFP4
 // block factor d (1 otherwise) and its E4M3 code.
-template <int KIND, bool DYN>
+template <int KIND, bool DYN, bool CODES = true>
 __device__ __forceinline__ float vec_scale(const TensorArgs& a, int64_t grow, int64_t b, int v,
                                            const float* f, float row_s, float t,
                                            float* dfac, uint32_t* bcode) {
@@ -43,7 +43,7 @@ __device__ __forceinline__ float vec_scale(const TensorArgs& a, int64_t grow, in
         } else {
             ratio = a.scale[grow * (a.cols >> 4) + (v >> 1)] / t;
         }
-        float d = e4m3_round(fminf(ratio, 448.0f), bcode);
+        float d = CODES ? e4m3_round(fminf(ratio, 448.0f), bcode) : e4m3_round(fminf(ratio, 448.0f));
         *dfac = d;
         return t * d;
     }
@@ -77,7 +77,10 @@ __device__ __forceinline__ float row_scale(const TensorArgs& a, int64_t grow, in
     return 0.0f;
 }
 
-template <int KIND, bool DYN>
+// CODES: the 4/8-bit codes (and NVFP4 block-scale codes) are formed only when
+// the caller asks for them; without them the per-element code logic is not
+// compiled in
+template <int KIND, bool DYN, bool CODES>
 __global__ __launch_bounds__(TPB) void k_tensor_fwd(TensorArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int64_t nrows = a.batch * a.rows;
@@ -95,24 +98,26 @@ __global__ __launch_bounds__(TPB) void k_tensor_fwd(TensorArgs a) {
             unpack8(xr[v], f);
             float dfac;
             uint32_t bc;
-            const float s = vec_scale<KIND, DYN>(a, grow, b, v, f, row_s, t, &dfac, &bc);
+            const float s = vec_scale<KIND, DYN, CODES>(a, grow, b, v, f, row_s, t, &dfac, &bc);
             float yv[8];
             uint32_t c4 = 0;
             uint32_t c8[2] = {0u, 0u};
             quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) {
                 yv[i] = e.q * s;
-                const uint32_t c = elem_code<KIND>(e, f[i]);
-                c4 |= (c & 0xFu) << (4 * i);
-                c8[i >> 2] |= (c & 0xFFu) << (8 * (i & 3));
+                if (CODES) {
+                    const uint32_t c = elem_code<KIND>(e, f[i]);
+                    c4 |= (c & 0xFu) << (4 * i);
+                    c8[i >> 2] |= (c & 0xFFu) << (8 * (i & 3));
+                }
             });
             if (a.y) reinterpret_cast<uint4*>(a.y + grow * a.cols)[v] = pack8(yv);
-            if (a.codes) {
+            if (CODES && a.codes) {
                 if (four_bit)
                     reinterpret_cast<uint32_t*>(a.codes + grow * (a.cols >> 1))[v] = c4;
                 else
                     reinterpret_cast<uint2*>(a.codes + grow * a.cols)[v] = make_uint2(c8[0], c8[1]);
             }
-            if (KIND == K_NVFP4 && a.bcodes && !(v & 1))
+            if (CODES && KIND == K_NVFP4 && a.bcodes && !(v & 1))
                 a.bcodes[grow * (a.cols >> 4) + (v >> 1)] = (uint8_t)bc;
         }
     }
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(TPB) void k_tensor_bwd(TensorArgs a) {
             unpack8(xr[v], f);
             float dfac;
             uint32_t bc;
-            const float s = vec_scale<KIND, DYN>(a, grow, b, v, f, row_s, t, &dfac, &bc);
+            const float s = vec_scale<KIND, DYN, false>(a, grow, b, v, f, row_s, t, &dfac, &bc);
             float gx[8];
             float part = 0.0f;
             quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) {
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(TPB) void k_tensor_bwd(TensorArgs a) {
 // for NVFP4 block scales and per-group scales, whose index is the vector's
 // flat index over 2 or group/8: blocks and groups align with lane pairs and
 // lane groups because the row length is a multiple of the block or group.
-template <int KIND, bool DYN>
+template <int KIND, bool DYN, bool CODES = true>
 __device__ __forceinline__ float flat_scale(const TensorArgs& a, int64_t gv, int sh, const float* f, float t,
                                             uint32_t* bc) {
     if (KIND == K_NVFP4) {
@@ -211,6 +216,10 @@ __device__ __forceinline__ float flat_scale(const TensorArgs& a, int64_t gv, int
         } else {
             ratio = a.scale[gv >> 1] / t;
         }
+        if (!CODES) {
+            *bc = 0;
+            return t * e4m3_round(fminf(ratio, 448.0f));
+        }
         return t * e4m3_round(fminf(ratio, 448.0f), bc);
     }
     *bc = 0;
@@ -218,7 +227,7 @@ __device__ __forceinline__ float flat_scale(const TensorArgs& a, int64_t gv, int
     return a.scale[gv >> sh];
 }
 
-template <int KIND, bool DYN>
+template <int KIND, bool DYN, bool CODES>
 __global__ __launch_bounds__(TPB) void k_tensor_fwd_flat(TensorArgs a) {
     const int64_t per = a.rows * (a.cols >> 3);             // vectors per matrix
     const int64_t b = blockIdx.y;
@@ -231,22 +240,24 @@ __global__ __launch_bounds__(TPB) void k_tensor_fwd_flat(TensorArgs a) {
         float f[8];
         unpack8(reinterpret_cast<const uint4*>(a.x)[gv], f);
         uint32_t bc;
-        const float s = flat_scale<KIND, DYN>(a, gv, sh, f, t, &bc);
+        const float s = flat_scale<KIND, DYN, CODES>(a, gv, sh, f, t, &bc);
         float yv[8];
         uint32_t c4 = 0;
         uint32_t c8[2] = {0u, 0u};
         quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) {
             yv[i] = e.q * s;
-            const uint32_t c = elem_code<KIND>(e, f[i]);
-            c4 |= (c & 0xFu) << (4 * i);
-            c8[i >> 2] |= (c & 0xFFu) << (8 * (i & 3));
+            if (CODES) {
+                const uint32_t c = elem_code<KIND>(e, f[i]);
+                c4 |= (c & 0xFu) << (4 * i);
+                c8[i >> 2] |= (c & 0xFFu) << (8 * (i & 3));
+            }
         });
         if (a.y) reinterpret_cast<uint4*>(a.y)[gv] = pack8(yv);
-        if (a.codes) {
+        if (CODES && a.codes) {
             if (four_bit) reinterpret_cast<uint32_t*>(a.codes)[gv] = c4;
             else reinterpret_cast<uint2*>(a.codes)[gv] = make_uint2(c8[0], c8[1]);
         }
-        if (KIND == K_NVFP4 && a.bcodes && !(gv & 1)) a.bcodes[gv >> 1] = (uint8_t)bc;
+        if (CODES && KIND == K_NVFP4 && a.bcodes && !(gv & 1)) a.bcodes[gv >> 1] = (uint8_t)bc;
     }
 }
 
@@ -270,7 +281,7 @@ __global__ __launch_bounds__(TPB) void k_tensor_bwd_flat(TensorArgs a) {
         float f[8];
         unpack8(reinterpret_cast<const uint4*>(a.x)[gv], f);
         uint32_t bc;
-        const float s = flat_scale<KIND, DYN>(a, gv, sh, f, t, &bc);
+        const float s = flat_scale<KIND, DYN, false>(a, gv, sh, f, t, &bc);
         float gx[8];
         float part = 0.0f;
         quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) {
@@ -356,10 +367,17 @@ size_t tensor_workspace_bytes(const QParams& q, int64_t batch, int64_t rows) {
     default: if (dyn) LAUNCH(KERNEL, K_FP8, true); else LAUNCH(KERNEL, K_FP8, false); break;          \
     }
 
+#define FQ_LAUNCH_C(KERNEL, KIND, DYN)                                                     \
+    do {                                                                                   \
+        if (codes) FQ_LAUNCH_GRID(KERNEL, KIND, DYN, true);                                \
+        else FQ_LAUNCH_GRID(KERNEL, KIND, DYN, false);                                     \
+    } while (0)
+
 hipError_t launch_tensor_fwd(const TensorArgs& a, hipStream_t st) {
     const int64_t nrows = a.batch * a.rows;
     if (nrows == 0 || a.cols == 0) return hipSuccess;
     const bool dyn = a.q.source == S_DYNAMIC;
+    const bool codes = a.codes || a.bcodes;
     switch (a.q.kind) {
     case K_NONE: {
         if (!a.y || a.y == a.x) return hipSuccess;
@@ -372,8 +390,18 @@ hipError_t launch_tensor_fwd(const TensorArgs& a, hipStream_t st) {
     case K_INT:
     case K_FP8:
         // NVFP4 blocks and groups flat; per-row / per-tensor scales a row per wave
-        if ((a.q.kind == K_NVFP4 || a.q.gran == G_GROUP) && a.batch <= 65535) { FQ_KINDS(k_tensor_fwd_flat, FQ_LAUNCH_FLAT) }
-        else { FQ_KINDS(k_tensor_fwd, FQ_LAUNCH) }
+        if ((a.q.kind == K_NVFP4 || a.q.gran == G_GROUP) && a.batch <= 65535) {
+#define FQ_LAUNCH_GRID(KERNEL, KIND, DYN, C)                                                \
+    hipLaunchKernelGGL((KERNEL<KIND, DYN, C>), dim3((unsigned)grid_flat(a.rows * (a.cols >> 3)), (unsigned)a.batch), \
+                       dim3(TPB), 0, st, a)
+            FQ_KINDS(k_tensor_fwd_flat, FQ_LAUNCH_C)
+#undef FQ_LAUNCH_GRID
+        } else {
+#define FQ_LAUNCH_GRID(KERNEL, KIND, DYN, C)                                                \
+    hipLaunchKernelGGL((KERNEL<KIND, DYN, C>), dim3((unsigned)grid_rows(a.batch * a.rows)), dim3(TPB), 0, st, a)
+            FQ_KINDS(k_tensor_fwd, FQ_LAUNCH_C)
+#undef FQ_LAUNCH_GRID
+        }
         break;
     default: return hipErrorInvalidValue;
     }
