@@ -35,8 +35,13 @@ CASES = [
     ("nvfp4_w_many", OP.NVFP4_W, (70000, 1, 32)),
     ("int4_g128_many", OP.INT4_G128, (66000, 1, 128)),
     ("fp8_row_many", OP.FP8_ROW, (66000, 2, 64)),
-    # a W2-shaped per-channel stack slice: rows of 768 (96 vectors)
+    # rows of 32 mod 64 vectors (768 columns: 96) take two rows per wave: even
+    # and odd row counts, per-tensor scales whose row pairs straddle two matrices
     ("int8_row_768", OP.INT8_ROW, (4, 6, 768)),
+    ("fp8_row_768_odd", OP.FP8_ROW, (3, 5, 768)),
+    ("int4_row_768", QSpec("int", "row", 0, "learnable", -8, 7), (2, 3, 768)),
+    ("fp8_tensor_768", OP.FP8_TENSOR, (2, 3, 768)),
+    ("int8_tensor_256_odd", QSpec("int", "tensor", 0, "learnable", -128, 127), (3, 7, 256)),
 ]
 
 
