@@ -352,7 +352,7 @@ def main():
     ap.add_argument("--stages", action="store_true", help="print per-stage times to stderr")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; the expert-parallel path over several GPUs "
+        print("bench.py: the library runs on one GPU; the expert-parallel path over several GPUs "
               "is designed but not built, so --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
