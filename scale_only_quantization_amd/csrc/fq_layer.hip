@@ -665,8 +665,10 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
 // ------------------------------------------- B7 A1 backward + unpermute-sum --
 // SPLIT waves per token, each on a contiguous 1/SPLIT of the row: the recomputed
 // codec terms depend only on 16-blocks or a per-expert scale, never on the
-// whole row, and half rows keep the wave's registers (and occupancy) in bounds.
-// The per-row partial of ds_a1 is then SPLIT partials, rowpart[row SPLIT + half].
+// whole row, and parts of a row keep the wave's registers (and occupancy) in
+// bounds; quarter rows (one vector per lane at H = 2048) double the waves in
+// flight over half rows.  The per-row partial of ds_a1 is then SPLIT
+// partials, rowpart[row SPLIT + part].
 template <int KIND, int NV, int SPLIT>
 __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
@@ -821,7 +823,8 @@ hipError_t launch_permute_a1(const PermuteArgs& a, hipStream_t st) {
     if (a.T == 0) return hipSuccess;
     const bool row_stat = a.a1.q.kind != K_NONE && a.a1.q.kind != K_NVFP4 && a.a1.q.gran == G_ROW &&
                           a.a1.q.source == S_DYNAMIC;
-    const int split = row_stat ? 1 : unpermute_split(a.H);
+    // half rows per wave (quarter rows measured slower here than in the backward)
+    const int split = row_stat ? 1 : ((a.H >> 3) % 128 == 0 && (a.H >> 3) >= 256 ? 2 : 1);
     const dim3 grid(grid_waves(a.T * split));
     const int nv = nv_for(a.H / split);
 #define FQ_PERM(KIND)                                                                                   \
@@ -929,8 +932,12 @@ hipError_t launch_swiglu_bwd(const SwigluBwdArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// waves per token in the A1 backward: a quarter row each when the row is a
+// multiple of 256 vectors (H = 2048: one vector per lane), else a half row
+// when a multiple of 128; each wave's ds_a1 partial is one of that many per row
 int unpermute_split(int H) {
     const int nvec = H >> 3;
+    if (nvec % 256 == 0) return 4;
     return (nvec % 128 == 0 && nvec >= 256) ? 2 : 1;
 }
 
@@ -939,8 +946,16 @@ hipError_t launch_unpermute_a1(const UnpermuteArgs& a, hipStream_t st) {
     const int split = unpermute_split(a.H);
     const dim3 grid(grid_waves(a.T * split));
     const int nv = nv_for(a.H / split);
+    const int nv4 = a.H / split <= 512 ? 1 : nv;
 #define FQ_UNPERM(KIND)                                                                                 \
-    if (split == 2) {                                                                                   \
+    if (split == 4) {                                                                                   \
+        switch (nv4) {                                                                                  \
+        case 1: hipLaunchKernelGGL((k_unpermute_a1<KIND, 1, 4>), grid, dim3(TPB), 0, st, a); break;     \
+        case 2: hipLaunchKernelGGL((k_unpermute_a1<KIND, 2, 4>), grid, dim3(TPB), 0, st, a); break;     \
+        case 4: hipLaunchKernelGGL((k_unpermute_a1<KIND, 4, 4>), grid, dim3(TPB), 0, st, a); break;     \
+        default: hipLaunchKernelGGL((k_unpermute_a1<KIND, 8, 4>), grid, dim3(TPB), 0, st, a); break;    \
+        }                                                                                               \
+    } else if (split == 2) {                                                                            \
         switch (nv) {                                                                                   \
         case 2: hipLaunchKernelGGL((k_unpermute_a1<KIND, 2, 2>), grid, dim3(TPB), 0, st, a); break;     \
         case 4: hipLaunchKernelGGL((k_unpermute_a1<KIND, 4, 2>), grid, dim3(TPB), 0, st, a); break;     \
