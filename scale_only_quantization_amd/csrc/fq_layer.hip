@@ -388,6 +388,32 @@ __device__ __forceinline__ float exp_neg(float g) {        // e^-g as the forwar
     return exp2_taylor(y);
 }
 
+// 1/d correctly rounded for d in [2^-120, 2^120]: one Newton step with FMAs
+// from the hardware reciprocal (within an ulp); on gfx950 this equals the IEEE
+// reciprocal for every significand at every exponent of that range.
+__device__ __forceinline__ float rcp_rn(float d) {
+    const float y0 = __builtin_amdgcn_rcpf(d);
+    return __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
+}
+
+// silu(g) = g / den with den = 1 + e^-g, correctly rounded.  With den <= 2^120
+// and |g| >= 2^-100 the quotient and the FMA remainder stay normal, so
+// Markstein's correction of g RN(1/den) is the rounded quotient; g = +-0 gives
+// g RN(1/den) = +-0 exactly; anything else takes the IEEE division.
+// *sig = RN(1/den) (the sigmoid) when den <= 2^120.
+__device__ __forceinline__ float silu_div(float g, float den, float* sig) {
+    if (den <= 0x1p120f) {
+        const float inv = rcp_rn(den);
+        *sig = inv;
+        const float q0 = g * inv;
+        if (g == 0.0f) return q0;
+        if (fabsf(g) >= 0x1p-100f) return __builtin_fmaf(__builtin_fmaf(-q0, den, g), inv, q0);
+        return g / den;
+    }
+    *sig = 1.0f / den;
+    return g / den;
+}
+
 // ------------------------------------------------------------- F5 SwiGLU+A2 --
 // RW rows per wave: with RW = 2 (used when a row has 32 mod 64 vectors of 8)
 // the wave's vectors u = lane + 64 c run over both rows, row u / nvec, so no
@@ -421,7 +447,10 @@ __global__ __launch_bounds__(TPB) void k_swiglu_a2(SwigluArgs a) {
                 unpack8(zr[v], g);
                 unpack8(zr[v + nvec], uu);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) h[i] = (g[i] / (1.0f + exp_neg(g[i]))) * uu[i];
+                for (int i = 0; i < 8; ++i) {
+                    float sig;
+                    h[i] = silu_div(g[i], 1.0f + exp_neg(g[i]), &sig) * uu[i];
+                }
                 hv[c] = pack8(h);
                 unpack8(hv[c], h);                       // h as stored (bf16)
             } else {
@@ -605,18 +634,11 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float den = 1.0f + exp_neg(g[i]);
-                const float inv = 1.0f / den;                // sigmoid(g), correctly rounded
-                sg[i] = inv;
-                // g / den correctly rounded, as the forward forms it: from the
-                // reciprocal by the corrected division while den <= 2^120
-                float sl;
-                if (den <= 0x1p120f) {
-                    const float q0 = g[i] * inv;
-                    sl = __builtin_fmaf(__builtin_fmaf(-q0, den, g[i]), inv, q0);
-                } else {
-                    sl = g[i] / den;
-                }
+                // sigmoid(g) = RN(1/den) and g / den correctly rounded, as the
+                // forward forms them
+                float sig;
+                const float sl = silu_div(g[i], 1.0f + exp_neg(g[i]), &sig);
+                sg[i] = sig;
                 h[i] = sl * u[i];
             }
             if (recompute) {
