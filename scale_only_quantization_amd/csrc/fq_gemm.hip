@@ -710,12 +710,20 @@ hipError_t launch(const GemmArgs& g, hipStream_t st) {
 }
 
 // out[o] = sum of `per` consecutive partials (fixed order), o < n_out
-// out[o] = sum of part[o * per .. o * per + per): L = pow2 >= per (<= 64)
-// lanes per output read its partials coalesced, lane j taking j, j + L, ...,
-// then a fixed xor tree over the L lanes (deterministic)
-__global__ __launch_bounds__(256) void k_sg_sum(const float* part, int64_t n_out, int per, float* out) {
+// lanes per output of k_sg_sum: one for a few partials (a thread reads its
+// run of <= 16 floats), else the power of two >= per, at most 64
+__host__ __device__ __forceinline__ int sg_sum_lanes(int per) {
     int L = 1;
-    while (L < per && L < 64) L <<= 1;
+    if (per > 16)
+        while (L < per && L < 64) L <<= 1;
+    return L;
+}
+
+// out[o] = sum of part[o * per .. o * per + per): L lanes per output read its
+// partials coalesced, lane j taking j, j + L, ..., then a fixed xor tree over
+// the L lanes (deterministic)
+__global__ __launch_bounds__(256) void k_sg_sum(const float* part, int64_t n_out, int per, float* out) {
+    const int L = sg_sum_lanes(per);
     const int lane = threadIdx.x & 63;
     const int64_t o = ((int64_t)blockIdx.x * 256 + threadIdx.x) / L;
     const int j0 = lane & (L - 1);
@@ -756,9 +764,7 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st) {
 
 // blocks of k_sg_sum for n_out outputs of `per` partials each
 static unsigned sg_sum_blocks(int64_t n_out, int per) {
-    int64_t L = 1;
-    while (L < per && L < 64) L <<= 1;
-    return (unsigned)((n_out * L + 255) / 256);
+    return (unsigned)((n_out * sg_sum_lanes(per) + 255) / 256);
 }
 
 int sg_mode(const QParams& q) {
