@@ -47,15 +47,36 @@ WORKLOADS = {
 DX_STAGES = ("fc1_dgrad", "unpermute_a1", "a1_sum")
 
 
-def stage_work(L, fmt, full_bwd=True):
-    """Algorithmic bytes (HBM kernels) or FLOPs (GEMMs) of each stage per launch;
-    without the full backward, permute_dy forms no d topk_w (no read of Y_r)."""
-    E, H, I, T, k = L.E, L.H, L.I, L.T, L.k
+def _scale_elems(q, rows, cols):
+    """Scale elements one [rows, cols] matrix reads under descriptor q (along cols)."""
+    from scale_only_quantization_amd import fqlib as F
+    if q.kind == F.FQ_NONE or q.source == F.FQ_DYNAMIC:
+        return 0
+    if q.kind == F.FQ_NVFP4:
+        return rows * (cols // 16)
+    if q.gran == F.FQ_PER_GROUP:
+        return rows * (cols // q.group)
+    return rows if q.gran == F.FQ_PER_ROW else 1
+
+
+def _scale_grad_fused(q):
+    """True where the weight-gradient GEMM's epilogue writes the scale gradient
+    itself (NVFP4 blocks, INT groups of 16), so no reduction stage follows."""
+    from scale_only_quantization_amd import fqlib as F
+    return q.kind == F.FQ_NVFP4 or (q.gran == F.FQ_PER_GROUP and q.group == 16)
+
+
+def stage_work(dims, descs, full_bwd=True):
+    """Algorithmic bytes (HBM kernels) or FLOPs (GEMMs) of each stage per launch,
+    for layer sizes `dims` (E, H, I, T, k) and quantiser descriptors
+    (w1, w2, a1, a2); without the full backward, permute_dy forms no d topk_w
+    (no read of Y_r)."""
+    E, H, I, T, k = dims.E, dims.H, dims.I, dims.T, dims.k
+    w1q, w2q = descs[0], descs[1]
     R = T * k
     bf, f4 = 2, 4
-    nv = fmt.startswith("nvfp4")
-    sw1 = E * 2 * I * (H // 16 if nv else (H // 128 if "w4" in fmt else 1)) * f4
-    sw2 = E * H * (I // 16 if nv else (I // 128 if "w4" in fmt else 1)) * f4
+    sw1 = E * _scale_elems(w1q, 2 * I, H) * f4
+    sw2 = E * _scale_elems(w2q, H, I) * f4
     W1, W2 = E * 2 * I * H * bf, E * H * I * bf
     fwd = {
         "route": ("hbm", R * 4 * 3),
@@ -78,10 +99,10 @@ def stage_work(L, fmt, full_bwd=True):
         "unpermute_a1": ("hbm", 2 * T * H * bf + R * H * bf),
         "a1_sum": ("hbm", R * 4),
         # the weight-scale gradients: formed in the weight-gradient GEMM's
-        # epilogue for nvfp4 (nothing left for this stage), else summed from
-        # its per-32-column partials (INT/FP8 per-row, per-group and per-tensor)
-        "w1_scale_grad": ("hbm", 0 if nv else W1 // 2 * 4 // 32 + sw1),
-        "w2_scale_grad": ("hbm", 0 if nv else W2 // 2 * 4 // 32 + sw2),
+        # epilogue for NVFP4 blocks and INT groups of 16 (nothing left for this
+        # stage), else summed from its per-32-column partials
+        "w1_scale_grad": ("hbm", 0 if _scale_grad_fused(w1q) else W1 // 2 * 4 // 32 + sw1),
+        "w2_scale_grad": ("hbm", 0 if _scale_grad_fused(w2q) else W2 // 2 * 4 // 32 + sw2),
     }
     return fwd, bwd
 
@@ -164,7 +185,7 @@ def sources_sha(kernel):
     return h.hexdigest()[:16]
 
 
-def scale_adamw_step(ev, F, dl, L, reps=20, warmup=3):
+def scale_adamw_step(ev, F, dl, reps=20, warmup=3):
     """The scale optimiser step (fq_scale_adamw) over the layer's learnable
     scales with the gradients of the last backward: NVFP4 block scales of both
     stacks (projected against their tensor scales) and the activation tensor
@@ -172,13 +193,14 @@ def scale_adamw_step(ev, F, dl, L, reps=20, warmup=3):
     update reads p, g, m, v and writes p, m, v (28 B)."""
     import torch
     params, keep, count = [], [], 0
-    for n, q in (("w1", L.w1), ("w2", L.w2), ("a1", L.a1), ("a2", L.a2)):
+    for n, q in dl.q.items():
         g = dl.g.get("ds_" + n)
         if g is None:
             continue
         p = dl.d["s_" + n]
         m, v = torch.zeros_like(p), torch.zeros_like(p)
-        t = dl.d.get("t_" + n) if n.startswith("w") and q.kind == "nvfp4" else None
+        # NVFP4 weight block scales are projected against their tensor scale
+        t = dl.d.get("t_" + n) if n.startswith("w") and q.kind == F.FQ_NVFP4 else None
         per = p.numel() // t.numel() if t is not None else 1
         keep += [m, v]
         params.append(F.scale_param(p, g, m, v, t, per))
@@ -249,28 +271,28 @@ def distill_logits(ev, F, T=16384, V=151936, k=64, reps=5, warmup=2):
 def fake_quant_stack(ev, F, reps=20, warmup=3):
     """Standalone fq_tensor on the weight-only microbench stack: 128 expert
     matrices 768 x 2048 bf16 N(0, 0.02) with 0.1% outliers x 20, NVFP4 block-16
-    and INT4 group-128 with learnable fp32 scales; forward (y), then the
-    straight-through scale gradient from an fp32 upstream gradient.  Per call:
-    average over `reps` back-to-back calls between two events."""
+    and INT4 group-128 with learnable fp32 scales (the weight quantisers of the
+    library's nvfp4 and w4a16 presets); forward (y), then the straight-through
+    scale gradient from an fp32 upstream gradient.  Per call: average over
+    `reps` back-to-back calls between two events."""
     import torch
 
     import synth
-    from oracle import presets as OP
-    from tests.fq_testutil import qdesc_of, to_dev_bf16
+    from scale_only_quantization_amd.layer import bf16_to_device
     W, G = synth.make_weight_stack()
     E, N, K = W.shape
     n = W.size
-    x = to_dev_bf16(W)
+    x = bf16_to_device(W)
     g = torch.from_numpy(G).cuda()
     del G
     y = torch.empty_like(x)
     out = {}
-    for name, q, kind in (("nvfp4", OP.NVFP4_W, "nvfp4"), ("int4_g128", OP.INT4_G128, "int4_g")):
-        c = synth.calibrate_weight(kind, W, group=128)
+    for name, fmt, kind in (("nvfp4", "nvfp4", "nvfp4"), ("int4_g128", "w4a16", "int4_g")):
+        qd = F.preset(fmt)[0]
+        c = synth.calibrate_weight(kind, W, group=qd.group)
         s = torch.from_numpy(c["s"]).cuda()
         t = torch.from_numpy(c["t"]).cuda() if "t" in c else None
         ds = torch.empty_like(s)
-        qd = qdesc_of(q)
         nscale = s.numel() * 4
         e0, e1 = ev.create(2)
         res = {}
@@ -294,17 +316,44 @@ def fake_quant_stack(ev, F, reps=20, warmup=3):
     return out
 
 
+def host_environment():
+    """The host CPU: its model, usable cores, numpy and its BLAS."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = {}
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = dict(name=b.get("name"), version=b.get("version"), config=b.get("openblas configuration"))
+    except Exception:
+        pass
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            threads = max(i.get("num_threads", 1) for i in info)
+            blas["runtime"] = f"{info[0].get('internal_api')} {info[0].get('version')}"
+    except Exception:
+        pass
+    return dict(cpu_model=model, affinity_cores=len(os.sched_getaffinity(0)), blas_threads=threads,
+                numpy=np.__version__, blas=blas)
+
+
 def cpu_baseline(data, P, fmt, quantiles=tuple(np.linspace(0.02, 0.98, 25))):
     """Time the oracle (numpy, float64 GEMMs) on a bounded sample: the full forward
     and backward of a few experts, i.e. every routed row of those experts, as a
     sub-layer with one routing slot per row."""
     from oracle import layer as OL
     from oracle import presets as OP
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    env = host_environment()
+    cores = env["blas_threads"] or env["affinity_cores"]
     case = data["case"]
     ids, w = data["ids"], data["w"]
     counts = np.bincount(ids.ravel(), minlength=case.E)
@@ -336,71 +385,57 @@ def cpu_baseline(data, P, fmt, quantiles=tuple(np.linspace(0.02, 0.98, 25))):
     OL.backward(Ls, Ps, S, dY, ws)
     dt = time.perf_counter() - t0
     tokens = t.size / case.k
-    return dict(value=tokens / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+    return dict(value=tokens / dt, unit="tokens/s", cores=int(cores), kind="oracle", host=env,
                 sample=(f"full fwd+bwd of experts {picks} (rows {[int(counts[e]) for e in picks]}, "
                         f"{t.size} routed rows = {tokens:.0f} token-equivalents at top-{case.k}) "
                         f"in {dt:.1f} s"))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stages", action="store_true", help="print per-stage times to stderr")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py: the library runs on one GPU; the expert-parallel path over several GPUs "
-              "is designed but not built, so --gpus must be 1", file=sys.stderr)
-        sys.exit(2)
-
+def run_layer(name, F, ev, steps, warmup, data=None):
+    """One layer workload: seeded inputs, the device layer built from the
+    library's preset of its format, `warmup` untimed and `steps` timed
+    forward + backward steps, per-stage times and the dominant kernel's
+    roofline.  Returns (result, layer, data, params)."""
     import torch
 
     import synth
-    from tests.layer_run import DeviceLayer, spec_for
-    from scale_only_quantization_amd import fqlib as F
+    from scale_only_quantization_amd.layer import ExpertLayer, LayerDims
 
-    case_name, fmt, desc, full_bwd = WORKLOADS[args.workload]
+    case_name, fmt, desc, full_bwd = WORKLOADS[name]
     case = synth.CASES[case_name]
     t_gen = time.perf_counter()
-    data = synth.make_layer(case)
+    if data is None:
+        data = synth.make_layer(case)
     P = synth.layer_params(data, fmt)
-    print(f"[bench] inputs for {args.workload} generated in {time.perf_counter() - t_gen:.1f} s",
-          file=sys.stderr, flush=True)
-    L = spec_for(fmt, case.E, case.H, case.I, case.T, case.k)
-    dl = DeviceLayer(L, data, P)
-    ev = HipEvents()
+    print(f"[bench] inputs for {name} ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+    dims = LayerDims(case.E, case.H, case.I, case.T, case.k)
+    dl = ExpertLayer(dims, fmt, data["W1"], data["W2"], data["X"], data["ids"], data["w"], data["dY"], P)
     nf, nb = len(F.FWD_STAGES) + 1, len(F.BWD_STAGES) + 1
-    evf = [ev.create(nf) for _ in range(args.steps)]
-    evb = [ev.create(nb) for _ in range(args.steps)]
+    evf = [ev.create(nf) for _ in range(steps)]
+    evb = [ev.create(nb) for _ in range(steps)]
 
     def step(i=None):
-        F.fwd(dl.desc, dl.P, dl.d["X"], dl.d["ids"], dl.d["w"], dl.y, dl.saved, dl.ws,
-              events=None if i is None else evf[i])
-        F.bwd(dl.desc, dl.P, dl.d["X"], dl.d["ids"], dl.d["w"], dl.d["dY"], dl.saved,
-              dl.dx if full_bwd else None, dl.dw if full_bwd else None,
-              dl.G, dl.ws, events=None if i is None else evb[i])
+        dl.forward(events=None if i is None else evf[i])
+        dl.backward(dx=full_bwd, dw=full_bwd, events=None if i is None else evb[i])
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms = elapsed * 1e3 / args.steps
+    ms = elapsed * 1e3 / steps
     value = case.T / (ms / 1e3)
 
     # per-stage durations (ms), averaged over the timed steps
-    names = [("fwd", n) for n in F.FWD_STAGES] + [("bwd", n) for n in F.BWD_STAGES]
     dur = {}
-    for pass_, stages, evs in (("fwd", F.FWD_STAGES, evf), ("bwd", F.BWD_STAGES, evb)):
-        for si, n in enumerate(stages):
+    for stages_, evs in ((F.FWD_STAGES, evf), (F.BWD_STAGES, evb)):
+        for si, n in enumerate(stages_):
             dur[n] = float(np.mean([ev.elapsed_ms(e[si], e[si + 1]) for e in evs]))
-    work_f, work_b = stage_work(L, fmt, full_bwd)
+    work_f, work_b = stage_work(dims, tuple(dl.q[n] for n in ("w1", "w2", "a1", "a2")), full_bwd)
     work = {**work_f, **work_b}
     if not full_bwd:
         for n in DX_STAGES:
@@ -428,38 +463,84 @@ def main():
         ach = amount / (avg_ms * 1e-3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
     roof = dict(bound="mfma" if kind == "mfma" else "hbm", achieved=round(ach, 1), peak=peak, unit=unit,
-                frac=round(ach / peak, 4), traffic=traffic_from_profiles(dom, args.workload),
+                frac=round(ach / peak, 4), traffic=traffic_from_profiles(dom, name),
                 kernel=dom, launches=list(launches), avg_launch_ms=round(avg_ms, 4),
                 work_per_launch=amount)
+    config = {"workload": desc, "format": fmt, "experts": case.E, "hidden": case.H,
+              "intermediate": case.I, "tokens": case.T, "topk": case.k, "routing": case.routing,
+              "backward": "full: dX, d topk_w and every scale gradient" if full_bwd
+              else "weight-scale gradients only"}
+    res = dict(ms_per_step=round(ms, 4), value=round(value, 1), steps=steps, warmup=warmup, config=config,
+               roofline=roof, stages=stages)
+    return res, dl, data, P
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the w8a8, w4afp8 and fp8 layers after the headline nvfp4 layer")
+    ap.add_argument("--stages", action="store_true", help="print per-stage times to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: the library runs on one GPU; the expert-parallel path over several GPUs "
+              "is designed but not built, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from scale_only_quantization_amd import fqlib as F
+
+    ev = HipEvents()
+    res, dl, data, P = run_layer(args.workload, F, ev, args.steps, args.warmup)
     if args.stages:
         for n in F.FWD_STAGES + F.BWD_STAGES:
-            print(f"[bench] {n:14s} {stages.get(n, 'not run')}", file=sys.stderr)
+            print(f"[bench] {n:14s} {res['stages'].get(n, 'not run')}", file=sys.stderr)
 
     out = {
         "metric": "expert-layer fwd+bwd tokens/s",
-        "value": round(value, 1),
+        "value": res["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": desc, "format": fmt, "experts": case.E, "hidden": case.H,
-                   "intermediate": case.I, "tokens": case.T, "topk": case.k, "routing": case.routing,
-                   "backward": "full: dX, d topk_w and every scale gradient" if full_bwd
-                   else "weight-scale gradients only"},
-        "roofline": roof,
-        "stages": stages,
+        "config": res["config"],
+        "roofline": res["roofline"],
+        "stages": res["stages"],
     }
-    out["scale_adamw"] = scale_adamw_step(ev, F, dl, L)
+    out["scale_adamw"] = scale_adamw_step(ev, F, dl)
     if args.stages:
         print(f"[bench] scale_adamw {out['scale_adamw']}", file=sys.stderr)
     del dl
     torch.cuda.empty_cache()
+    if args.workload == "qwen3" and not args.no_workloads:
+        # the other layer workloads, each in its own format; T = 32768 inputs
+        # are drawn once for w4afp8 and fp8
+        out["workloads"] = {}
+        shared = None
+        for name in ("qwen3_w8a8", "qwen3_w4afp8", "qwen3_fp8"):
+            r, wl, d, _ = run_layer(name, F, ev, min(args.steps, 10), min(args.warmup, 3),
+                                    data=shared if WORKLOADS[name][0] == "qwen3l" else None)
+            shared = d if WORKLOADS[name][0] == "qwen3l" else shared
+            out["workloads"][name] = dict(
+                ms_per_step=r["ms_per_step"], value=r["value"], unit="tokens/s", steps=r["steps"],
+                tokens=r["config"]["tokens"], format=r["config"]["format"], roofline=r["roofline"],
+                stages={n: s["frac"] for n, s in r["stages"].items()})
+            print(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step, {r['value'] / 1e6:.3f} M tokens/s",
+                  file=sys.stderr, flush=True)
+            del wl, d
+            torch.cuda.empty_cache()
+        del shared
     print("[bench] weight-only fake-quant microbench ...", file=sys.stderr, flush=True)
     out["fake_quant"] = fake_quant_stack(ev, F)
     if args.stages:
@@ -469,8 +550,8 @@ def main():
     if args.stages:
         print(f"[bench] distill {out['distill']}", file=sys.stderr)
     if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on a bounded sample ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(data, P, fmt)
+        print("[bench] timing the CPU baseline on a bounded sample ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(data, P, WORKLOADS[args.workload][1])
     print(json.dumps(out), flush=True)
 
 
