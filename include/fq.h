@@ -161,9 +161,10 @@ size_t fq_tensor_workspace_size(const fq_qdesc* q, int64_t batch, int64_t rows, 
  * topk_ids / topk_w are inputs (nxmr.cn article, section 二.3).  A quantiser
  * with kind FQ_NONE is the identity, so all-FQ_NONE is the BF16 teacher forward
  * (AngelSlim page, opening paragraph).
- * silu(g) = g / (1 + 2^(-g log2 e)) with 2^y evaluated as 2^rint(y) times the
- * degree-7 Taylor polynomial of 2^f, f = y - rint(y), each step one fp32
- * operation without fusion.
+ * silu(g) = g / (1 + e^-g) is evaluated in fp32 to within (8 + 2|g|) 2^-24 of
+ * its exact value, relative (results below 2^-126 within that plus a subnormal
+ * ulp); h therefore equals bf16 of the exact product except where the exact
+ * value lies that close to a bf16 rounding midpoint.
  */
 typedef struct {
     int64_t E;        /* experts, 1..1024                                        */

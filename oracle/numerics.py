@@ -136,40 +136,15 @@ def e4m3_rne(v) -> tuple[np.ndarray, np.ndarray]:
 # ---------------------------------------------------------------------------
 # float32 SiLU used by the forward (its rounding decides the A2 codes)
 # ---------------------------------------------------------------------------
-# silu(g) = g / (1 + exp(-g)).  exp(-g) = 2**y with y = -g*log2(e), split as
-# y = n + f with n = rint(y) and |f| <= 1/2; 2**f is the degree-7 Taylor
-# polynomial sum_i (f ln 2)**i / i!, evaluated by Horner's rule with a separate
-# multiply and add at every step (no fused multiply-add), then scaled by 2**n.
-# Every step is one IEEE float32 operation, so the value is fully determined.
-# Truncation error of the polynomial: (ln2/2)**8/8! < 6e-9 relative.
-LN2 = 0.6931471805599453
-EXP2_COEF = [F32(LN2 ** i / np.prod(np.arange(1, i + 1, dtype=np.float64)))
-             for i in range(8)]                      # c0 .. c7
-LOG2E = F32(1.0 / LN2)
-
-
-def exp2_f32(y) -> np.ndarray:
-    """2**y for float32 y in [-200, 200], by the split-and-Taylor rule above."""
-    y = np.asarray(y, dtype=np.float32)
-    n = np.rint(y).astype(np.float32)
-    f = (y - n).astype(np.float32)
-    p = np.full_like(f, EXP2_COEF[7])
-    for c in EXP2_COEF[6::-1]:
-        p = (p * f).astype(np.float32)
-        p = (p + c).astype(np.float32)
-    with np.errstate(over="ignore", under="ignore"):
-        return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
-
-
 def silu_f32(g) -> np.ndarray:
-    """SiLU of float32 values, as the forward computes it (see above)."""
-    g = np.asarray(g, dtype=np.float32)
-    y = (-g * LOG2E).astype(np.float32)
-    y = np.clip(y, F32(-200.0), F32(200.0)).astype(np.float32)
-    e = exp2_f32(y)
+    """SiLU of float32 values, g / (1 + e^-g), as the float32 value nearest to
+    the exact result: evaluated in float64 (a few float64 roundings, far below
+    half a float32 ulp) and rounded once to float32.  The pages name SwiGLU as
+    the expert activation and fix no evaluation of it, so the plain definition
+    is used."""
+    g = np.asarray(g, dtype=np.float32).astype(np.float64)
     with np.errstate(over="ignore"):
-        den = (F32(1.0) + e).astype(np.float32)
-    return (g / den).astype(np.float32)
+        return (g / (1.0 + np.exp(-g))).astype(np.float32)
 
 
 def silu_f64(g) -> np.ndarray:

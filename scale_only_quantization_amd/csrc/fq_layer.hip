@@ -366,9 +366,12 @@ __global__ __launch_bounds__(TPB) void k_permute_a1(PermuteArgs a) {
 }
 
 // ------------------------------------------------------------------ SiLU ----
-// silu(g) = g / (1 + 2^y), y = -g log2(e): 2^y = 2^rint(y) * P(y - rint(y)),
-// P the degree-7 Taylor polynomial of 2^f (coefficients (ln 2)^i / i!, rounded
-// to fp32), Horner with separate multiply and add.
+// silu(g) = g / (1 + e^-g) in fp32, within (8 + 2|g|) 2^-24 of the exact value
+// (relative; results below 2^-126 within that plus (1 + |g|) 2^-149).
+// e^-|g| = 2^y, y = -|g| log2(e) clamped at -200 (2^-200 is 0 in fp32):
+// 2^y = 2^rint(y) * P(y - rint(y)), P the degree-7 Taylor polynomial of 2^f
+// (coefficients (ln 2)^i / i!, rounded to fp32), Horner with separate multiply
+// and add; the 2|g| term is the rounding of y.
 __device__ __forceinline__ float exp2_taylor(float y) {
     const float n = rintf(y);
     const float f = y - n;
@@ -382,11 +385,6 @@ __device__ __forceinline__ float exp2_taylor(float y) {
     p = p * f; p = p + 1.0f;
     return ldexpf(p, (int)n);
 }
-__device__ __forceinline__ float exp_neg(float g) {        // e^-g as the forward defines it
-    float y = (-g) * 0x1.715476p+0f;
-    y = fminf(fmaxf(y, -200.0f), 200.0f);
-    return exp2_taylor(y);
-}
 
 // 1/d correctly rounded for d in [2^-120, 2^120]: one Newton step with FMAs
 // from the hardware reciprocal (within an ulp); on gfx950 this equals the IEEE
@@ -396,22 +394,24 @@ __device__ __forceinline__ float rcp_rn(float d) {
     return __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
 }
 
-// silu(g) = g / den with den = 1 + e^-g, correctly rounded.  With den <= 2^120
-// and |g| >= 2^-100 the quotient and the FMA remainder stay normal, so
-// Markstein's correction of g RN(1/den) is the rounded quotient; g = +-0 gives
-// g RN(1/den) = +-0 exactly; anything else takes the IEEE division.
-// *sig = RN(1/den) (the sigmoid) when den <= 2^120.
-__device__ __forceinline__ float silu_div(float g, float den, float* sig) {
-    if (den <= 0x1p120f) {
-        const float inv = rcp_rn(den);
-        *sig = inv;
-        const float q0 = g * inv;
-        if (g == 0.0f) return q0;
-        if (fabsf(g) >= 0x1p-100f) return __builtin_fmaf(__builtin_fmaf(-q0, den, g), inv, q0);
-        return g / den;
-    }
-    *sig = 1.0f / den;
-    return g / den;
+// silu(g) and sigmoid(g), as the forward and the backward both form them,
+// without branches and without overflow: with e = e^-|g| in [0, 1] and
+// den = 1 + e in [1, 2],
+//     g >= 0:  silu = g / den,      sigmoid = 1 / den
+//     g <  0:  silu = g e / den,    sigmoid = e / den
+// (both are g / (1 + e^-g)).  The quotient is Markstein's correction of
+// num RN(1/den) (the rounded quotient while it is normal); the sign is g's,
+// so silu(-0) = -0.
+__device__ __forceinline__ float silu_sig(float g, float* sig) {
+    const float e = exp2_taylor(fmaxf(-fabsf(g) * 0x1.715476p+0f, -200.0f));
+    const float den = 1.0f + e;
+    const float inv = rcp_rn(den);
+    const float sel = g < 0.0f ? e : 1.0f;
+    const float num = g * sel;
+    const float q0 = num * inv;
+    const float r = __builtin_fmaf(__builtin_fmaf(-q0, den, num), inv, q0);
+    *sig = sel * inv;
+    return __builtin_copysignf(r, g);
 }
 
 // ------------------------------------------------------------- F5 SwiGLU+A2 --
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(TPB) void k_swiglu_a2(SwigluArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     float sig;
-                    h[i] = silu_div(g[i], 1.0f + exp_neg(g[i]), &sig) * uu[i];
+                    h[i] = silu_sig(g[i], &sig) * uu[i];
                 }
                 hv[c] = pack8(h);
                 unpack8(hv[c], h);                       // h as stored (bf16)
@@ -632,15 +632,9 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) { g[i] = 0.0f; u[i] = 0.0f; dh[i] = 0.0f; }
             }
+            // silu and sigmoid as the forward forms them
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                // sigmoid(g) = RN(1/den) and g / den correctly rounded, as the
-                // forward forms them
-                float sig;
-                const float sl = silu_div(g[i], 1.0f + exp_neg(g[i]), &sig);
-                sg[i] = sig;
-                h[i] = sl * u[i];
-            }
+            for (int i = 0; i < 8; ++i) h[i] = silu_sig(g[i], &sg[i]) * u[i];
             if (recompute) {
                 float hq[8];
                 unpack8(pack8(h), hq);                       // h as the forward stored it

@@ -105,13 +105,16 @@ class ExpertLayer:
         self.y = torch.empty((dims.T, dims.H), dtype=torch.bfloat16, device="cuda")
         self.dx = torch.empty((dims.T, dims.H), dtype=torch.bfloat16, device="cuda")
         self.dw = torch.empty((dims.T, dims.k), dtype=torch.float32, device="cuda")
-        # one gradient per trainable scale, shaped like the parameter it belongs to
+        # one gradient per trainable scale, shaped like the parameter it belongs
+        # to: the scale tensor, or the tensor scale t of NVFP4 weights with
+        # dynamic block factors (an activation's NVFP4 tensor scale is its s_a)
         self.g = {}
         for n, q in self.q.items():
-            src = self.d["s_" + n]
+            dyn_w = n.startswith("w") and q.kind == F.FQ_NVFP4 and q.source == F.FQ_DYNAMIC
+            src = self.d[("t_" if dyn_w else "s_") + n]
             if has_param(q):
                 if src is None:
-                    raise ValueError(f"quantiser {n} has a trainable scale but no s_{n} was given")
+                    raise ValueError(f"quantiser {n} has a trainable scale but none was given")
                 self.g["ds_" + n] = torch.empty(src.shape, dtype=torch.float32, device="cuda")
             else:
                 self.g["ds_" + n] = None

@@ -34,6 +34,38 @@ def test_library_exports_every_declared_function():
     assert F.lib().fq_abi_version() == 1
 
 
+def _header_enums():
+    """name -> value of every enumerator and #define constant fq.h declares."""
+    src = open(os.path.join(ROOT, "include", "fq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for body in re.findall(r"enum\s*\{(.*?)\}", src, flags=re.S):
+        for name, val in re.findall(r"\b(FQ_[A-Z0-9_]+)\s*=\s*(-?\d+)", body):
+            out[name] = int(val)
+    for name, val in re.findall(r"#define\s+(FQ_[A-Z0-9_]+)\s+(-?\d+)", src):
+        out[name] = int(val)
+    return out
+
+
+def test_binding_enums_match_the_header():
+    # every constant the binding mirrors has the value fq.h gives it
+    h = _header_enums()
+    mirrored = {n: getattr(F, n) for n in dir(F) if n.startswith("FQ_") and isinstance(getattr(F, n), int)}
+    assert len(mirrored) >= 20
+    for n, v in mirrored.items():
+        assert n in h, f"{n} is not declared in fq.h"
+        assert h[n] == v, (n, h[n], v)
+    for n, v in F.FORMATS.items():
+        assert h["FQ_FMT_" + n.upper()] == v
+    for n, v in F.BUFFERS.items():
+        assert h["FQ_BUF_" + n.upper()] == v
+    for n, v in F.DISTILL_TYPES.items():
+        assert h["FQ_DISTILL_" + n.upper()] == v
+    # the values the design notes record where the ABI departs from the survey's sketch
+    assert (h["FQ_NONE"], h["FQ_NVFP4"], h["FQ_INT"], h["FQ_FP8E4M3"]) == (0, 1, 2, 3)
+    assert (h["FQ_LEARNABLE"], h["FQ_STATIC"], h["FQ_DYNAMIC"]) == (0, 1, 2)
+
+
 @pytest.mark.parametrize("fmt", list(OP.PRESETS))
 def test_presets_match_oracle(fmt):
     got = F.preset(fmt)

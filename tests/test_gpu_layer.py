@@ -3,7 +3,10 @@ the C ABI) against the oracle.
 
 Stage-wise: each stage's oracle is fed the device's own inputs, so codes,
 permutations, fake-quant outputs, the combine and the unpermute are bit-exact,
-GEMM outputs within 1e-2 and scale gradients within 2e-3.  End-to-end: scale
+GEMM outputs within 1e-2 and scale gradients within 2e-3.  H^ follows the
+kernel's SiLU, which is within a few float32 ulps of the oracle's correctly
+rounded one: it is bit-exact except for a counted, bounded number of elements
+one grid step apart.  End-to-end: scale
 gradients against the oracle's full chain within 2e-3."""
 import numpy as np
 import pytest
@@ -12,8 +15,8 @@ import synth
 from oracle import codec, layer as OL, presets as OP, routing
 from oracle.codec import QSpec
 from oracle.numerics import F32, bf16_rne
-from tests.fq_testutil import (assert_array_equal, assert_bits_equal, check_gemm, check_scale_grad,
-                               torch)
+from tests.fq_testutil import (assert_array_equal, assert_bits_equal, assert_fake_quant_near_bits,
+                               check_gemm, check_scale_grad, torch)
 from tests.layer_run import DeviceLayer, spec_for
 
 pytestmark = pytest.mark.gpu
@@ -81,10 +84,12 @@ def _full_parity(L, data, P, Po, end_to_end=True):
         assert_bits_equal(Xh[rows], a1["y"][0], f"X^ expert {e}")
         # F4: fc1 on the device's own operands
         check_gemm(Z1[rows], OL.gemm_nt(Xh[rows], W1h[e]), f"Z1 expert {e}")
-        # F5: SwiGLU + A2 from the device's Z1, bit-exact
+        # F5: SwiGLU + A2 from the device's Z1: bit-exact but for the rare
+        # elements where the kernel's SiLU and the correctly rounded one put h
+        # on different sides of a bf16 rounding midpoint (counted, bounded)
         h = OL.stage_swiglu(Z1[rows], I)
         a2 = OL.stage_act_quant(L.a2, h, sa2, e)
-        assert_bits_equal(Hh[rows], a2["y"][0], f"H^ expert {e}")
+        assert_fake_quant_near_bits(Hh[rows], a2, L.a2, f"H^ expert {e}")
         # F6
         check_gemm(Yr[rows], OL.gemm_nt(Hh[rows], W2h[e]), f"Y_r expert {e}")
         # B2, B3
@@ -241,6 +246,52 @@ def test_layer_dynamic_weight_quantisers():
     L = OL.LayerSpec(4, 256, 256, 37, 3, QSpec("int", "row", 0, "dynamic", -128, 127),
                      QSpec("int", "group", 32, "dynamic", -8, 7), a1, a2)
     P = dict(s_w1=None, t_w1=None, s_w2=None, t_w2=None, s_a1=None, s_a2=None)
+    Po = dict(P, W1=data["W1"], W2=data["W2"])
+    _full_parity(L, data, P, Po)
+
+
+def _calibrate(q, W):
+    """Initial parameters of weight quantiser q over W [E, N, K] from amax
+    statistics: (scale or None, NVFP4 tensor scale or None)."""
+    a = np.abs(np.asarray(W, np.float32))
+    E, N, K = a.shape
+    mat = a.reshape(E, -1).max(1)
+    if q.kind == "nvfp4":
+        return None, (mat / np.float32(2688)).astype(np.float32)       # dynamic blocks: t only
+    top = np.float32(448.0 if q.kind == "fp8" else q.qmax)
+    if q.gran == "tensor":
+        s = mat
+    elif q.gran == "row":
+        s = a.max(-1)
+    else:
+        s = a.reshape(E, N, K // q.group, q.group).max(-1)
+    return np.maximum(s / top, np.float32(1e-6)).astype(np.float32), None
+
+
+WEIGHT_QUANTISERS = {
+    # per-tensor learnable scales: the epilogue's per-32-column partials summed per row, then per matrix
+    "fp8-tensor": QSpec("fp8", "tensor", 0, "learnable"),
+    "int8-tensor": QSpec("int", "tensor", 0, "learnable", -128, 127),
+    # INT groups: 16 written by the epilogue itself, 64 from its partials, 8 through a stored dW^
+    "int4-g16": QSpec("int", "group", 16, "learnable", -8, 7),
+    "int8-g64": QSpec("int", "group", 64, "learnable", -128, 127),
+    "int4-g8": QSpec("int", "group", 8, "learnable", -8, 7),
+    # NVFP4 with dynamic block factors: the learnable tensor scale, through a stored dW^
+    "nvfp4-dynamic": QSpec("nvfp4", "group", 16, "dynamic"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WEIGHT_QUANTISERS))
+def test_layer_weight_quantiser_granularities(name):
+    # the weight-scale gradient paths outside the format presets, with bf16
+    # activations: 37 tokens x top-3 over 4 experts
+    q = WEIGHT_QUANTISERS[name]
+    case = synth.LayerCase("t", 4, 256, 256, 37, 3, "zipf", "nvfp4", 31)
+    data = synth.make_layer(case)
+    s1, t1 = _calibrate(q, data["W1"])
+    s2, t2 = _calibrate(q, data["W2"])
+    P = dict(s_w1=s1, t_w1=t1, s_w2=s2, t_w2=t2, s_a1=None, s_a2=None)
+    L = OL.LayerSpec(4, 256, 256, 37, 3, q, q, QSpec(), QSpec())
     Po = dict(P, W1=data["W1"], W2=data["W2"])
     _full_parity(L, data, P, Po)
 

@@ -9,8 +9,10 @@ The routing permutation is compared whole, bit for bit. The other outputs are
 compared on three experts: the most loaded, the least loaded non-empty one and
 the median. For each of them:
 
-  * the fake-quant weights, all routed rows of X^ and the sampled rows of H^
-    must be bit-exact;
+  * the fake-quant weights and all routed rows of X^ must be bit-exact;
+  * H^ must be bit-exact except for a counted, bounded number of elements one
+    grid step apart (the kernel's SiLU is within a few float32 ulps of the
+    oracle's correctly rounded one);
   * the GEMM outputs on sampled rows must be within 1e-2;
   * the weight- and activation-scale gradients, reduced over every row of the
     expert, must be within 2e-3.
@@ -24,8 +26,8 @@ import pytest
 
 import synth
 from oracle import codec, layer as OL, routing
-from tests.fq_testutil import (assert_array_equal, assert_bits_equal, check_gemm, check_scale_grad,
-                               torch)
+from tests.fq_testutil import (assert_array_equal, assert_bits_equal, assert_fake_quant_near_bits,
+                               check_gemm, check_scale_grad, torch)
 from tests.layer_run import DeviceLayer, spec_for
 
 pytestmark = pytest.mark.gpu
@@ -105,7 +107,7 @@ def test_full_size_layer_sampled(case_name, fmt):
         h = OL.stage_swiglu(Z1, I)
         a2 = OL.stage_act_quant(L.a2, h, sa2, e)
         Hh = _rows(dl, "hhat", allr, I)
-        assert_bits_equal(Hh, a2["y"][0], f"H^ expert {e}")
+        assert_fake_quant_near_bits(Hh, a2, L.a2, f"H^ expert {e}")
         check_gemm(_rows(dl, "yr", rows, H), OL.gemm_nt(Hh[s], W2h), f"Y_r expert {e}")
         # B1 on sampled rows
         dYr = _rows(dl, "dyr", allr, H)

@@ -156,6 +156,43 @@ def test_dynamic_int8_row_max_maps_to_127():
     assert np.all(np.abs(out["q"]) <= 127)
 
 
+def test_dynamic_fp8_row_max_maps_to_448():
+    # per-token FP8: the scale is the row's amax over the largest E4M3 value, so
+    # the row's largest element lands on +-448 (byte 0x7E | sign)
+    x = _rand((1, 64, 512), 17, scale=3.0)
+    out = codec.fake_quant(FP8_TOK, x)
+    i = np.abs(x).argmax(-1)
+    q = np.take_along_axis(out["q"], i[..., None], -1)[..., 0]
+    assert np.all(np.abs(q) == 448.0)
+    codes = np.take_along_axis(out["codes"], i[..., None], -1)[..., 0]
+    assert np.all((codes & 0x7F) == 0x7E)
+    # r of the amax element is 448 up to the two roundings of amax / 448 and x / s
+    assert np.all(np.abs(out["r"]) <= 448.0 * (1 + 2.0 ** -22))
+    # every row's scale is its own amax / 448, whatever the other rows hold
+    amax = np.abs(x).max(-1)
+    assert np.array_equal(out["shat"][..., 0], (amax / np.float32(448.0)).astype(np.float32))
+
+
+def test_dynamic_int_group_max_maps_to_qmax():
+    # per-group INT4 [-8, 7]: a group's largest element lands on +-7, the
+    # symmetric end of the range (the -8 code is never reached from the amax)
+    x = _rand((2, 16, 256), 18)
+    out = codec.fake_quant(INT4_DYN_G, x)
+    g = INT4_DYN_G.group
+    xs = np.abs(x).reshape(2, 16, 256 // g, g)
+    qs = out["q"].reshape(2, 16, 256 // g, g)
+    i = xs.argmax(-1)
+    q = np.take_along_axis(qs, i[..., None], -1)[..., 0]
+    assert np.all(np.abs(q) == 7.0)
+    assert np.all(qs >= -7) and np.all(qs <= 7)
+    # an INT8 group behaves the same with its own end, 127
+    q8 = QSpec("int", "group", 64, "dynamic", -128, 127)
+    out8 = codec.fake_quant(q8, x)
+    xs8 = np.abs(x).reshape(2, 16, 4, 64)
+    q8v = np.take_along_axis(out8["q"].reshape(2, 16, 4, 64), xs8.argmax(-1)[..., None], -1)[..., 0]
+    assert np.all(np.abs(q8v) == 127.0)
+
+
 def test_dynamic_nvfp4_block_max_range():
     x = _rand((1, 64, 256), 8)
     t = np.array([np.abs(x).max() / 2688], np.float32)

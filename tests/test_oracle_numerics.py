@@ -109,27 +109,54 @@ def test_bf16_rne_rounds_float64_once():
     assert nm.bf16_rne(np.array([1.0 + 3 * 2.0 ** -8]))[0] == np.float32(1.0 + 2.0 ** -6)
 
 
-def test_exp2_f32_accuracy():
-    y = np.linspace(-30, 30, 200001).astype(np.float32)
-    got = nm.exp2_f32(y).astype(np.float64)
-    ref = np.exp2(y.astype(np.float64))
-    assert np.max(np.abs(got / ref - 1)) < 4 * 2.0 ** -24
-    # exact powers of two
-    k = np.arange(-100, 100).astype(np.float32)
-    assert np.array_equal(nm.exp2_f32(k), np.ldexp(np.float32(1), k.astype(np.int32)))
+def _silu_decimal_f32(g):
+    """SiLU of one float32 value, computed with 50 significant decimal digits and
+    rounded to the nearest float32 (ties to even) by comparing against the exact
+    midpoints of the float32 neighbours."""
+    import decimal
+    if g > 1000:          # e^-g < 2^-1400: the quotient is g to far beyond float32 precision
+        return np.float32(g)
+    if g < -1000:         # |g| e^g < 2^-1400: below the smallest float32 subnormal
+        return np.float32(-0.0)
+    ctx = decimal.Context(prec=50, Emax=10 ** 6, Emin=-10 ** 6)
+    d = decimal.Decimal(float(g))
+    v = ctx.divide(d, ctx.add(decimal.Decimal(1), ctx.exp(-d)))
+    c = np.float32(float(v))
+    if v == 0:
+        return np.float32(np.copysign(0.0, g))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        err = abs(decimal.Decimal(float(cand)) - v)
+        if best is None or err < best[0] or (err == best[0] and (int(cand.view(np.uint32)) & 1) == 0):
+            best = (err, cand)
+    y = best[1]
+    return np.float32(-0.0) if y == 0 and g < 0 else y
 
 
-def test_silu_f32_accuracy_all_bf16():
+def test_silu_f32_is_correctly_rounded():
+    # a spread of bf16 inputs over the whole finite range, plus the edges of the
+    # sigmoid's saturation and of float32 underflow
     g = nm.all_bf16_values()
-    g = g[np.abs(g) < 1e4]
-    got = nm.silu_f32(g).astype(np.float64)
-    with np.errstate(over="ignore"):
-        ref = nm.silu_f64(g.astype(np.float64))
-    err = np.abs(got - ref)
-    # the float32 argument -g*log2(e) carries |g|-proportional rounding error
-    tol = (8 + 2 * np.abs(g.astype(np.float64))) * 2.0 ** -24 * np.abs(ref) + 1e-36   # exp(-g) overflows fp32 below g = -88
-    assert np.all(err <= tol)
-    assert nm.silu_f32(np.array([-200.0, -1e4], np.float32)).tolist() == [0.0, 0.0]
+    g = g[np.isfinite(g)]
+    pick = np.concatenate([g[::37], np.array([0.0, -0.0, 1e-30, -1e-30, 20.0, -20.0, 88.0, -88.0, -87.5,
+                                              -103.0, -104.0, -150.0, -200.0, 3.0e38, -3.0e38], np.float32)])
+    got = nm.silu_f32(pick)
+    for gi, yi in zip(pick, got):
+        ref = _silu_decimal_f32(gi)
+        assert yi.view(np.uint32) == np.float32(ref).view(np.uint32), (gi, yi, ref)
+
+
+def test_silu_f32_special_values():
+    v = nm.silu_f32(np.array([0.0, -0.0, 1.0e4, -1.0e4, -200.0], np.float32))
+    assert v[0] == 0 and v[1] == 0 and np.signbit(v[1])           # g / 2 keeps the sign of zero
+    assert v[2] == np.float32(1.0e4)                              # sigmoid saturates at 1
+    assert v[3] == 0 and np.signbit(v[3])                         # underflows to -0
+    assert v[4] == 0 and np.signbit(v[4])                         # -200 e^-200 is below float32 range
+    # silu(g) - silu(-g) = g holds exactly in the reals; after one rounding each
+    # side is within half an ulp
+    g = np.linspace(-10, 10, 4001).astype(np.float32)
+    d = nm.silu_f32(g).astype(np.float64) - nm.silu_f32(-g).astype(np.float64)
+    assert np.all(np.abs(d - g) <= np.spacing(np.abs(g).astype(np.float32)).astype(np.float64) + 1e-45)
 
 
 def test_dsilu_matches_finite_difference():
