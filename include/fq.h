@@ -13,7 +13,8 @@
  * Conventions for every entry point
  *   - Pointers marked "device" are HIP device pointers; "host" pointers are
  *     read before the call returns.  The caller owns every buffer; the library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no state between calls (one exception:
+ *     fq_scale_adamw_noalloc's fixed scratch array, described there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     All device work is enqueued on it asynchronously; nothing is synchronised
  *     and nothing is read back to the host.
@@ -323,6 +324,24 @@ size_t fq_scale_adamw_workspace_size(const fq_scale_param* params, int32_t npara
  * not 4-byte aligned (workspace: 8); FQ_E_WORKSPACE if workspace_bytes is short. */
 int fq_scale_adamw(const fq_scale_param* params, int32_t nparams, const fq_adamw_hparams* h, int64_t step,
                    float* grad_norm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same step with no workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing: its scratch
+ * (the norm pass's partials and the clip factor, 8 bytes per 32768 scale
+ * elements of each tensor, rounded up per tensor) is a fixed device array of
+ * FQ_SCALE_ADAMW_NOALLOC_MAX_BLOCKS + 1 doubles (256 KB + 8 B) inside the
+ * library, which every GPU the library runs on holds until the process ends.
+ * Each call on a GPU uses that GPU's one array, so calls that overlap on one
+ * GPU (different streams, or threads) race and must be ordered by the
+ * caller; results are otherwise identical, bit for bit, to fq_scale_adamw's.
+ * Errors: those of fq_scale_adamw (without the workspace ones), and
+ * FQ_E_WORKSPACE when the tensors need more than
+ * FQ_SCALE_ADAMW_NOALLOC_MAX_BLOCKS blocks (about 1.07e9 elements in all);
+ * FQ_E_HIP if the array's device address cannot be looked up. */
+#define FQ_SCALE_ADAMW_NOALLOC_MAX_BLOCKS 32768
+int fq_scale_adamw_noalloc(const fq_scale_param* params, int32_t nparams, const fq_adamw_hparams* h,
+                           int64_t step, float* grad_norm, void* stream);
 
 /* ---- distillation losses ---------------------------------------------------
  * The loss of quantisation-aware distillation on one batch of logits, and its

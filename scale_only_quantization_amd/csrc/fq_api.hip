@@ -5,6 +5,7 @@
 // error path is testable without a GPU), the layout of the saved and
 // workspace buffers, and the launch order of the forward and backward stages.
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "fq.h"
@@ -764,8 +765,19 @@ size_t fq_scale_adamw_workspace_size(const fq_scale_param* params, int32_t npara
     return round_up((size_t)(nb > 0 ? nb : 1) * sizeof(double) + sizeof(double), 256);
 }
 
-int fq_scale_adamw(const fq_scale_param* params, int32_t nparams, const fq_adamw_hparams* h, int64_t step,
-                   float* grad_norm, void* workspace, size_t workspace_bytes, void* stream) {
+// Scratch of fq_scale_adamw_noalloc: the norm pass's per-block partials and
+// the clip factor.  Every block of the norm pass writes its own partial and
+// the norm kernel writes the clip factor before the update reads it, so
+// nothing here needs clearing between calls.  In host code the name is only
+// a stand-in: kernels get the device address looked up per device below.
+static __device__ __align__(256) double scratch[FQ_SCALE_ADAMW_NOALLOC_MAX_BLOCKS + 1];
+
+namespace {
+
+// Validate one optimiser step and fill its launch arguments (all but the
+// scratch pointers); *nb receives the norm pass's block count.
+int adamw_args(const fq_scale_param* params, int32_t nparams, const fq_adamw_hparams* h, int64_t step,
+               float* grad_norm, AdamArgs* out, int64_t* nb_out) {
     if (!params || !h || nparams < 1 || nparams > FQ_MAX_SCALE_PARAMS || step < 1) return FQ_E_INVALID;
     const float hv[6] = {h->lr, h->beta1, h->beta2, h->eps, h->weight_decay, h->max_grad_norm};
     for (float v : hv)
@@ -792,8 +804,6 @@ int fq_scale_adamw(const fq_scale_param* params, int32_t nparams, const fq_adamw
         nb += adam_norm_blocks(q.count);
     }
     if (grad_norm && !aligned(grad_norm, 4)) return FQ_E_ALIGN;
-    if (!workspace || !aligned(workspace, 8)) return workspace ? FQ_E_ALIGN : FQ_E_WORKSPACE;
-    if (workspace_bytes < fq_scale_adamw_workspace_size(params, nparams)) return FQ_E_WORKSPACE;
     a.np = nparams;
     a.nb = nb;
     a.b1 = h->beta1;
@@ -807,9 +817,63 @@ int fq_scale_adamw(const fq_scale_param* params, int32_t nparams, const fq_adamw
     a.step_size = (float)((double)h->lr / bc1);
     a.bc2_sqrt = (float)std::sqrt(bc2);
     a.max_norm = h->max_grad_norm;
+    a.norm_out = grad_norm;
+    *out = a;
+    *nb_out = nb;
+    return FQ_OK;
+}
+
+constexpr int64_t NOALLOC_ADAM_BLOCKS = FQ_SCALE_ADAMW_NOALLOC_MAX_BLOCKS;
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+hipError_t scratch_on_current_device(double** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<double*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+int fq_scale_adamw(const fq_scale_param* params, int32_t nparams, const fq_adamw_hparams* h, int64_t step,
+                   float* grad_norm, void* workspace, size_t workspace_bytes, void* stream) {
+    AdamArgs a{};
+    int64_t nb = 0;
+    int s = adamw_args(params, nparams, h, step, grad_norm, &a, &nb);
+    if (s != FQ_OK) return s;
+    if (!workspace || !aligned(workspace, 8)) return workspace ? FQ_E_ALIGN : FQ_E_WORKSPACE;
+    if (workspace_bytes < fq_scale_adamw_workspace_size(params, nparams)) return FQ_E_WORKSPACE;
     a.part = static_cast<double*>(workspace);
     a.clip = reinterpret_cast<float*>(static_cast<double*>(workspace) + a.nb);
-    a.norm_out = grad_norm;
+    FQ_TRY(launch_scale_adamw(a, static_cast<hipStream_t>(stream)));
+    return FQ_OK;
+}
+
+int fq_scale_adamw_noalloc(const fq_scale_param* params, int32_t nparams, const fq_adamw_hparams* h,
+                           int64_t step, float* grad_norm, void* stream) {
+    AdamArgs a{};
+    int64_t nb = 0;
+    int s = adamw_args(params, nparams, h, step, grad_norm, &a, &nb);
+    if (s != FQ_OK) return s;
+    if (nb > NOALLOC_ADAM_BLOCKS) return FQ_E_WORKSPACE;
+    double* ptr = nullptr;
+    FQ_TRY(scratch_on_current_device(&ptr));
+    a.part = ptr;
+    a.clip = reinterpret_cast<float*>(ptr + a.nb);
     FQ_TRY(launch_scale_adamw(a, static_cast<hipStream_t>(stream)));
     return FQ_OK;
 }

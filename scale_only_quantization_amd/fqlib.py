@@ -76,6 +76,7 @@ class DistillDesc(Structure):
 DISTILL_TYPES = {"kl": 0, "rkl": 1, "cakld": 2, "topk_kl": 3}
 FQ_PROJ_POSITIVE, FQ_PROJ_E4M3_BLOCK = 0, 1
 FQ_MAX_SCALE_PARAMS = 16
+FQ_SCALE_ADAMW_NOALLOC_MAX_BLOCKS = 32768
 
 
 def _load():
@@ -114,6 +115,8 @@ def _load():
         "fq_scale_adamw_workspace_size": (c_size_t, [POINTER(ScaleParam), c_int32]),
         "fq_scale_adamw": (c_int32, [POINTER(ScaleParam), c_int32, POINTER(AdamWHparams), c_int64, c_void_p,
                                      c_void_p, c_size_t, c_void_p]),
+        "fq_scale_adamw_noalloc": (c_int32, [POINTER(ScaleParam), c_int32, POINTER(AdamWHparams), c_int64,
+                                             c_void_p, c_void_p]),
         "fq_distill_workspace_size": (c_size_t, [c_int64]),
         "fq_distill_loss": (c_int32, [POINTER(DistillDesc), c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
@@ -131,7 +134,8 @@ EXPORTS = ("fq_abi_version", "fq_status_string", "fq_last_hip_error", "fq_preset
            "fq_tensor_workspace_size", "fq_tensor", "fq_grouped_expert_saved_size",
            "fq_grouped_expert_workspace_size", "fq_grouped_expert_buffer",
            "fq_grouped_expert_fwd", "fq_grouped_expert_bwd", "fq_adamw_defaults",
-           "fq_scale_adamw_workspace_size", "fq_scale_adamw", "fq_distill_workspace_size", "fq_distill_loss")
+           "fq_scale_adamw_workspace_size", "fq_scale_adamw", "fq_scale_adamw_noalloc",
+           "fq_distill_workspace_size", "fq_distill_loss")
 
 
 def lib():
@@ -286,6 +290,14 @@ def scale_adamw(params, hp: AdamWHparams, step: int, grad_norm=None, workspace=N
     st = _lib.fq_scale_adamw(arr, len(params), ctypes.byref(hp), step, _ptr(grad_norm), _ptr(workspace),
                              _nbytes(workspace), _stream(stream))
     _check(st, "fq_scale_adamw")
+
+
+def scale_adamw_noalloc(params, hp: AdamWHparams, step: int, grad_norm=None, stream=None):
+    """The same step through fq_scale_adamw_noalloc: no workspace, the library's
+    fixed scratch array instead (calls on one GPU must not overlap)."""
+    arr = (ScaleParam * len(params))(*params)
+    st = _lib.fq_scale_adamw_noalloc(arr, len(params), ctypes.byref(hp), step, _ptr(grad_norm), _stream(stream))
+    _check(st, "fq_scale_adamw_noalloc")
 
 
 # --------------------------------------------------------- distillation loss --

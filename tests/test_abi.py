@@ -245,6 +245,26 @@ def test_scale_adamw_validation():
     assert _adam(ok, wsb=8) == F.FQ_E_WORKSPACE
 
 
+def test_scale_adamw_noalloc_validation():
+    # the same argument checks as the workspace form, then the size limit of the
+    # library's fixed scratch array, all before any HIP call
+    hp = F.adamw_defaults()
+
+    def noalloc(ps, step=1, norm=None):
+        arr = (F.ScaleParam * max(len(ps), 1))(*ps)
+        return F.lib().fq_scale_adamw_noalloc(arr, len(ps), ctypes.byref(hp), step, norm, None)
+    assert F.lib().fq_scale_adamw_noalloc(None, 1, ctypes.byref(hp), 1, None, None) == F.FQ_E_INVALID
+    assert noalloc([]) == F.FQ_E_INVALID
+    assert noalloc([_sp()], step=0) == F.FQ_E_INVALID
+    assert noalloc([_sp(g=None)]) == F.FQ_E_INVALID
+    assert noalloc([_sp(m=MIS)]) == F.FQ_E_ALIGN
+    assert noalloc([_sp()], norm=MIS) == F.FQ_E_ALIGN
+    chunk = 32768                              # scale elements per block of the norm pass
+    big = F.FQ_SCALE_ADAMW_NOALLOC_MAX_BLOCKS * chunk
+    assert noalloc([_sp(n=big + 1)]) == F.FQ_E_WORKSPACE
+    assert noalloc([_sp(n=big // 2), _sp(n=big // 2 + 1)]) == F.FQ_E_WORKSPACE
+
+
 def _dl(d, T=4, V=64, zs=FAKE, zt=FAKE, tv=None, ti=None, lab=None, loss=FAKE, rows=None, grad=None,
         ws=FAKE, wsb=1 << 16):
     return F.lib().fq_distill_loss(ctypes.byref(d), T, V, zs, zt, tv, ti, lab, loss, rows, grad, ws, wsb, None)
