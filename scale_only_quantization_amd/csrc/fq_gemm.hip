@@ -15,7 +15,9 @@
 // bounded to the valid rows, so rows past the routed rows or past an expert's
 // rows (the WGRAD reduction tail) read as zero.  A reduction step is BK deep;
 // S LDS stages are in flight, so a tile's loads are issued S-1 steps before
-// its MFMAs.
+// its MFMAs.  The stages of A come first in LDS, then those of B.  The large
+// FWD and DGRAD tiles run a ping-pong schedule (two groups of four waves, one
+// phase apart; see mainloop_pp).
 //   K-contiguous operand: LDS [rows][BK], the 16-B chunk index XORed with a
 //     row swizzle; a fragment (8 consecutive k of one row) is one
 //     ds_read_b128, and the 16 rows of one read pass fall on distinct banks.
@@ -44,8 +46,8 @@
 #define GEMM_WVM 2          // waves of the large tile along rows x columns
 #define GEMM_WVN 4
 #endif
-#ifndef GEMM_SCHED
-#define GEMM_SCHED 2        // 2: per sub-step the next reads, then the MFMAs; 1, 3: interleaved
+#ifndef GEMM_PP
+#define GEMM_PP 1           // ping-pong schedule of the 8-wave tile (FWD, DGRAD)
 #endif
 
 namespace fq {
@@ -73,19 +75,22 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 // K-contiguous operand tile [ROWS][BK]: element (row, k) at byte row*ld2 + 2k
 // of the resource.  Rows of 2 BK bytes; each 1-KB wave load covers 512/BK rows.
-// Swizzle: chunk ^ (row >> 2) & 3 for 64-B rows, chunk ^ (row ^ row >> 3) & 7
-// for 128-B rows, so the 16 rows one ds_read_b128 pass serves (16 lanes x 16 B,
-// 64 banks) fall on distinct banks.
+// Swizzle: chunk ^ (row >> 2) & 3 for 64-B rows, chunk ^ (row >> 1) & 7 for
+// 128-B rows, so the 16 rows one ds_read_b128 pass serves (16 lanes x 16 B,
+// 64 banks) fall on distinct banks; rows 32 apart share a swizzle, so a
+// wave's fragments of one k sub-step differ by constant offsets.
 template <int ROWS, int BK, int NW>
 struct KTile {
     static constexpr int BYTES = ROWS * BK * 2;
     static constexpr int PER_WAVE = BYTES / 1024 / NW;
     static constexpr int CPR = BK / 8;                 // 16-B chunks per row
+    static constexpr int RB = 2 * BK;                  // bytes per row
+    static constexpr int KS = BK / 16;                 // 16-deep sub-steps per step
     __device__ static __forceinline__ int swz(int row) {
-        return BK == 32 ? ((row >> 2) & 3) : ((row ^ (row >> 3)) & 7);
+        return BK == 32 ? ((row >> 2) & 3) : ((row >> 1) & 7);
     }
     __device__ static __forceinline__ int off(int row, int ch) {   // byte offset of 16-B chunk
-        return row * (2 * BK) + ((ch ^ swz(row)) << 4);
+        return row * RB + ((ch ^ swz(row)) << 4);
     }
     __amdgpu_buffer_rsrc_t rs;
     uint32_t voff[PER_WAVE];
@@ -113,6 +118,20 @@ struct KTile {
         return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
             tile + off(row, kk * 2 + (lane >> 5)));
     }
+    // A wave's fragments from per-lane offsets: one offset per sub-step kk for
+    // rows row0w + 32 t + lane%32 (row0w a multiple of 32); t adds 32 RB.
+    template <int WT>
+    struct Frags {
+        uint32_t o[KS];
+        __device__ __forceinline__ void prep(int row0w) {
+            const int lane = threadIdx.x & 63;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) o[kk] = (uint32_t)off(row0w + (lane & 31), kk * 2 + (lane >> 5));
+        }
+        __device__ __forceinline__ bf16x8 get(const lds_t* tile, int t, int kk) const {
+            return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(tile + o[kk] + t * 32 * RB);
+        }
+    };
 };
 
 // Row-contiguous operand tile [BK][ROWS] (stored as in memory): element
@@ -144,10 +163,10 @@ struct MNTile {
     }
     __device__ __forceinline__ void issue(lds_t* tile, int k0) {
         const int w = wave_id();
+        const uint32_t so = (uint32_t)k0 * ld2;          // wave-uniform: the scalar offset
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + w) * 1024, 16,
-                                                     voff[i] + (uint32_t)k0 * ld2, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + w) * 1024, 16, voff[i], so, 0, 0);
     }
     __device__ static __forceinline__ bf16x8 frag(const lds_t* tile, int row0, int kk) {
         const int lane = threadIdx.x & 63;
@@ -162,6 +181,30 @@ struct MNTile {
         const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(t + off(kb + 4, byte))));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+    // A wave's fragments from per-lane offsets: one offset per 32-row tile t
+    // (rows row0w + 32 t); sub-step kk adds 16 k-rows, the second read 4.
+    template <int WT>
+    struct Frags {
+        uint32_t o[WT];
+        __device__ __forceinline__ void prep(int row0w) {
+            const int lane = threadIdx.x & 63;
+            const int i = lane & 15;
+            const int kb = (lane >> 5) * 8 + (i >> 2);
+#pragma unroll
+            for (int t = 0; t < WT; ++t) {
+                const int mb = row0w + 32 * t + ((lane >> 4) & 1) * 16;
+                o[t] = (uint32_t)off(kb, (mb + 4 * (i & 3)) * 2);
+            }
+        }
+        __device__ __forceinline__ bf16x8 get(const lds_t* tile, int t, int kk) const {
+            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+            typedef __attribute__((address_space(3))) v4bf lds4;
+            lds_t* p = const_cast<lds_t*>(tile) + o[t] + kk * 16 * RB;
+            const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)p));
+            const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(p + 4 * RB)));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
 };
 
 // Block -> tile with XCD locality: workgroups are dealt to the 8 XCDs (each
@@ -395,11 +438,14 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
     constexpr int BM = 32 * WTM * WVM, BN = 32 * WTN * WVN;
     typedef typename std::conditional<MODE == WGRAD, MNTile<BM, BK, NW>, KTile<BM, BK, NW>>::type ATile;
     typedef typename std::conditional<MODE == FWD, KTile<BN, BK, NW>, MNTile<BN, BK, NW>>::type BTile;
-    constexpr int A_BYTES = ATile::BYTES, STAGE = ATile::BYTES + BTile::BYTES;
+    constexpr int A_BYTES = ATile::BYTES, B_BYTES = BTile::BYTES;
     constexpr int LOADS = ATile::PER_WAVE + BTile::PER_WAVE;     // wave load instructions per stage
+    constexpr int KS = BK / 16;                                  // 16-deep sub-steps per step
     static_assert(S >= 2 && S <= 4, "stages");
-    // the stages; FWD/DGRAD reuse them for the bf16 output tile
-    constexpr int SMEM = (MODE != WGRAD && BM * BN * 2 > S * STAGE) ? BM * BN * 2 : S * STAGE;
+    // LDS: the S stages of A, then the S stages of B (a stage's offset then
+    // fits a read's immediate); FWD/DGRAD reuse it for the bf16 output tile
+    constexpr int STAGES = S * (A_BYTES + B_BYTES);
+    constexpr int SMEM = (MODE != WGRAD && BM * BN * 2 > STAGES) ? BM * BN * 2 : STAGES;
     __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
     lds_t* smem = (lds_t*)smem_raw;
     const int lane = threadIdx.x & 63;
@@ -408,6 +454,10 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
 
     ATile la;
     BTile lb;
+    // this wave's fragment offsets inside a stage (formed at the start of each
+    // main loop, so they are not live across the weight-gradient epilogue)
+    typename ATile::template Frags<WTM> fa;
+    typename BTile::template Frags<WTN> fb;
     f32x16 acc[WTM][WTN];
     auto zero_acc = [&]() {
 #pragma unroll
@@ -417,20 +467,22 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
     };
+    auto stage_a = [&](int kt) { return smem + (kt % S) * A_BYTES; };
+    auto stage_b = [&](int kt) { return smem + S * A_BYTES + (kt % S) * B_BYTES; };
 
     // MFMAs of one BK-deep step: fragments of the next 16-deep sub-step are
     // read while the current sub-step's MFMAs run.
-    auto compute = [&](const lds_t* st) {
-        const lds_t* sa = st;
-        const lds_t* sb = st + A_BYTES;
+    auto compute = [&](int kt) {
+        const lds_t* sa = stage_a(kt);
+        const lds_t* sb = stage_b(kt);
         bf16x8 af[2][WTM], bfr[2][WTN];
 #pragma unroll
-        for (int kk = 0; kk <= BK / 16; ++kk) {
-            if (kk < BK / 16) {
+        for (int kk = 0; kk <= KS; ++kk) {
+            if (kk < KS) {
 #pragma unroll
-                for (int t = 0; t < WTM; ++t) af[kk & 1][t] = ATile::frag(sa, wm * 32 * WTM + t * 32, kk);
+                for (int t = 0; t < WTM; ++t) af[kk & 1][t] = fa.get(sa, t, kk);
 #pragma unroll
-                for (int t = 0; t < WTN; ++t) bfr[kk & 1][t] = BTile::frag(sb, wn * 32 * WTN + t * 32, kk);
+                for (int t = 0; t < WTN; ++t) bfr[kk & 1][t] = fb.get(sb, t, kk);
             }
             if (kk > 0) {
                 const int s = (kk - 1) & 1;
@@ -445,46 +497,18 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         constexpr int NR = WTM * (std::is_same<ATile, KTile<BM, BK, NW>>::value ? 1 : 2) +
                            WTN * (std::is_same<BTile, KTile<BN, BK, NW>>::value ? 1 : 2);
         constexpr int NM = WTM * WTN;
-        if (GEMM_SCHED == 2) {
-            // each sub-step: the next sub-step's reads first, then its MFMAs
+        // each sub-step: the next sub-step's reads first, then its MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+        for (int kk = 0; kk < KS - 1; ++kk) {
             __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-            for (int kk = 0; kk < BK / 16 - 1; ++kk) {
-                __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-        } else if (GEMM_SCHED == 3) {
-            // each sub-step: its MFMAs alternating with the next sub-step's reads
-            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-            for (int kk = 0; kk < BK / 16 - 1; ++kk) {
-#pragma unroll
-                for (int r = 0; r < NM; ++r) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (r < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-        } else if (GEMM_SCHED) {
-            // sub-step 0 reads, then each sub-step's MFMAs interleaved with the
-            // next sub-step's reads (a row-contiguous fragment is two reads)
-            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-            for (int kk = 0; kk < BK / 16 - 1; ++kk) {
-#pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, NM / NR > 0 ? NM / NR : 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            }
             __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
     };
-    auto stage = [&](int s) { return smem + (s % S) * STAGE; };
     auto issue = [&](int kt) {
-        la.issue(stage(kt), kt * BK);
-        lb.issue(stage(kt) + A_BYTES, kt * BK);
+        la.issue(stage_a(kt), kt * BK);
+        lb.issue(stage_b(kt), kt * BK);
     };
     // the first S-1 steps in flight
     auto prologue = [&](int nk) {
@@ -493,6 +517,8 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             if (p < nk) issue(p);
     };
     auto mainloop = [&](int nk) {
+        fa.prep(wm * 32 * WTM);
+        fb.prep(wn * 32 * WTN);
         for (int kt = 0; kt < nk; ++kt) {
             // this wave's loads of step kt are done once at most the loads of the
             // S-2 later steps are outstanding; the barrier then covers every wave
@@ -506,8 +532,98 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
             // the stage step kt+S-1 overwrites was read in step kt-1, finished by every wave
             if (kt + S - 1 < nk) issue(kt + S - 1);
-            compute(stage(kt));
+            compute(kt);
         }
+    };
+
+    // Ping-pong schedule of the 8-wave tile with 2 LDS stages.  Waves 0-3
+    // (group 0) and 4-7 (group 1), one of each per SIMD, alternate between a
+    // memory phase (every fragment of one BK step read from LDS into
+    // registers, and this wave's global loads) and a compute phase (that
+    // step's MFMAs from registers), group 1 one phase behind.  Between two
+    // barriers one wave on each SIMD issues MFMAs while the other reads LDS and
+    // waits on memory, so the matrix core does not idle across the barrier and
+    // the fragment reads that follow it.
+    //   group 0, memory phase of step kt: its loads of step kt+1 (into the
+    //     stage step kt-1 used, read by both groups in the two phases before),
+    //     then its fragment reads of step kt; it waits for those loads after
+    //     its next compute phase.
+    //   group 1, memory phase of step kt: its fragment reads of step kt, then
+    //     (once they have returned) its loads of step kt+2 into the same stage
+    //     (group 0 read it one phase earlier), then it waits for its loads of
+    //     step kt+1.
+    // Every load of step kt+1 has landed before the barrier that opens group
+    // 0's memory phase of step kt+1.  pre0: every wave's loads of step 0 were
+    // issued before the call (and LDS stage 1 may still be in use until the
+    // first barrier).
+    // (the weight gradient keeps the single-phase loop: with both operands
+    // read transposed its memory phase outlasts a compute phase; measured
+    // 7-12% slower)
+    constexpr bool PP = GEMM_PP && NW == 8 && S == 2 && WVM == 2 && MODE != WGRAD;
+    auto mainloop_pp = [&](int nk, bool pre0) {
+        const int grp = wave_id() >> 2;
+        bf16x8 af[KS][WTM], bfr[KS][WTN];
+        fa.prep(wm * 32 * WTM);
+        fb.prep(wn * 32 * WTN);
+        auto bar = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        if (!pre0) {
+            issue(0);
+            if (grp == 1 && nk > 1) {
+                issue(1);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            bar();
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            bar();
+            if (grp == 1 && nk > 1) issue(1);
+        }
+        if (grp == 1) bar();
+        auto phases = [&](int kt, int st) {
+            // memory phase
+            if (grp == 0 && kt + 1 < nk) issue(kt + 1);
+            const lds_t* sa = smem + st * A_BYTES;
+            const lds_t* sb = smem + 2 * A_BYTES + st * B_BYTES;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+                for (int t = 0; t < WTM; ++t) af[kk][t] = fa.get(sa, t, kk);
+#pragma unroll
+                for (int t = 0; t < WTN; ++t) bfr[kk][t] = fb.get(sb, t, kk);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (grp == 1) {
+                if (kt + 2 < nk) {
+                    issue(kt + 2);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+            }
+            bar();
+            // compute phase
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+                for (int ti = 0; ti < WTM; ++ti)
+#pragma unroll
+                    for (int tj = 0; tj < WTN; ++tj)
+                        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][tj], af[kk][ti], acc[ti][tj],
+                                                                              0, 0, 0);
+            if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            bar();
+        };
+        for (int kt = 0; kt < nk; kt += 2) {
+            phases(kt, 0);
+            if (kt + 1 < nk) phases(kt + 1, 1);
+        }
+        if (grp == 0) bar();
     };
 
     if constexpr (MODE != WGRAD) {
@@ -529,8 +645,12 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         else
             lb.init(make_rsrc(Be + n0, ((int64_t)g.K - 1) * g.ldb * 2 + (int64_t)BN * 2), g.ldb);
         zero_acc();
-        prologue(nk);
-        mainloop(nk);
+        if constexpr (PP) {
+            mainloop_pp(nk, false);
+        } else {
+            prologue(nk);
+            mainloop(nk);
+        }
         // Epilogue through LDS, so that global stores are whole row segments:
         // lane holds C[m = lane%32][n = 8*(v/4) + 4*(lane/32) + v%4] of each
         // 32x32 tile; it is written as bf16 into an LDS tile [BM][BN] whose
@@ -597,14 +717,17 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         setup(slot);
         prologue(nk);
         // the fused epilogue's weights go through the stage the next tile's
-        // first loads leave free (stage 1), two 4-KB slots per wave
-        constexpr bool LDS_EPI = S == 2 && WTN == 2 && WTM >= 2 && STAGE >= NW * 8192;
+        // first loads leave free (stage 1 of A for waves 0-3, of B for waves
+        // 4-7), two 4-KB slots per wave
+        constexpr bool LDS_EPI = S == 2 && WTN == 2 && WTM >= 2 && NW == 8 && A_BYTES >= 4 * 8192 &&
+                                 B_BYTES >= 4 * 8192;
         const int wu = wave_id();                     // wave-uniform: LDS base and resource
-        lds_t* wslots = smem + STAGE + wu * 8192;
+        lds_t* wslots = wu < 4 ? smem + A_BYTES + wu * 8192 : smem + 2 * A_BYTES + B_BYTES + (wu - 4) * 8192;
         WStage ws;
         for (;;) {
             zero_acc();
-            mainloop(nk);
+            if constexpr (PP) mainloop_pp(nk, true);
+            else mainloop(nk);
             __syncthreads();          // LDS stages free; every wave has read s_slot
             if (LDS_EPI && g.sg.out) {
                 ws.init(g.sg.W + ((int64_t)e * g.N + i0 + (wu / WVN) * 32 * WTM) * g.K + n0 + (wu % WVN) * 32 * WTN,
