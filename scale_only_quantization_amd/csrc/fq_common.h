@@ -65,35 +65,42 @@ __device__ __forceinline__ float group_sum(float v, int lanes) {
 }
 
 // ----------------------------------------------------------------- grids ---
-// E4M3FN round-to-nearest-even of a magnitude in [0, 448] (callers saturate
-// first).  Returns the value; *code gets the 7-bit magnitude code.  Both the
-// subnormal (spacing 2^-9 below 2^-6) and the normal rounding are formed and
-// one is selected, so lanes never diverge.
+// Round to nearest, ties to even, onto the E4M3FN and E2M1 grids with the
+// gfx950 conversion instructions (v_cvt_pk_fp8_f32 / v_cvt_f32_fp8 and
+// v_cvt_scalef32_pk_fp4_f32 / v_cvt_scalef32_pk_f32_fp4 with scale 1).  On the
+// box they agree bit for bit with the closed-form rounding (E4M3: subnormal
+// spacing 2^-9 below 2^-6, three mantissa bits above; E2M1: spacing 0.5 below
+// 2, 1 in [2, 4), 2 in [4, 6]) for every fp32 magnitude up to the largest
+// grid value, subnormals and ties included.  Callers saturate first.
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+
+// E4M3FN value of a magnitude in [0, 448]; *code gets the 7-bit magnitude code.
 __device__ __forceinline__ float e4m3_round(float a, uint32_t* code) {
-    const float m = rintf(a * 512.0f);                 // exact scaling, ties to even
-    uint32_t u = __float_as_uint(a);
-    u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;   // keep 3 mantissa bits
-    const bool sub = a < 0.015625f;
-    *code = sub ? (uint32_t)m : ((((u >> 23) - 120u) << 3) | ((u >> 20) & 7u));   // 8 == 2^-6, code 0x08
-    return sub ? m * 0.001953125f : __uint_as_float(u);
+    const int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, a, 0, false);
+    *code = (uint32_t)p & 0x7Fu;
+    return __builtin_amdgcn_cvt_f32_fp8(p, 0);
 }
 __device__ __forceinline__ float e4m3_round(float a) {
-    const float m = rintf(a * 512.0f);
-    uint32_t u = __float_as_uint(a);
-    u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
-    return a < 0.015625f ? m * 0.001953125f : __uint_as_float(u);
+    return __builtin_amdgcn_cvt_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(a, a, 0, false), 0);
+}
+// two at once (one conversion each way for the pair)
+__device__ __forceinline__ void e4m3_round2(float a0, float a1, float* q0, float* q1) {
+    const int p = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+    *q0 = __builtin_amdgcn_cvt_f32_fp8(p, 0);
+    *q1 = __builtin_amdgcn_cvt_f32_fp8(p, 1);
 }
 
-// E2M1 round-to-nearest-even of a magnitude in [0, 6]: spacing 0.5 below 2,
-// 1 in [2, 4), 2 in [4, 6]; rint breaks ties to the even multiple, which is
-// the even code.
-// Computed as (a + C) - C with C = 2^22, 2^23, 2^24 for spacing 0.5, 1, 2:
-// the fp32 sum rounds a to a multiple of ulp(C), ties to the even multiple;
-// C = 2^(21 + clamp(exponent of a, 1, 3)) with a = m 2^e, m in [0.5, 1).
+// E2M1 value of a magnitude in [0, 6]; ties go to the even code.
 __device__ __forceinline__ float e2m1_round(float a) {
-    const int e = __builtin_amdgcn_frexp_expf(a);
-    const float c = __uint_as_float((uint32_t)(min(max(e, 1), 3) + 148) << 23);   // 2^(21 + e)
-    return (a + c) - c;
+    const unsigned p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, a, 1.0f, 0);
+    const f32x2_cvt b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
+    return b.x;
+}
+__device__ __forceinline__ void e2m1_round2(float a0, float a1, float* q0, float* q1) {
+    const unsigned p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a0, a1, 1.0f, 0);
+    const f32x2_cvt b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
+    *q0 = b.x;
+    *q1 = b.y;
 }
 // 3-bit magnitude code of an E2M1 grid value: from 1 up, exponent and top
 // mantissa bit of the fp32 pattern; below 1 (0 or 0.5), 2 qm read off the low
@@ -108,13 +115,22 @@ __device__ __forceinline__ uint32_t e2m1_code(float qm) {
 // r = x / s correctly rounded, given inv = 1/s correctly rounded and s in the
 // normal range [2^-120, 2^120] (Markstein's correction step: q0 = x*inv, the
 // exact remainder x - q0*s by FMA, one corrected rounding).
+// 1/d correctly rounded for d in [2^-120, 2^120]: one Newton step with FMAs
+// from the hardware reciprocal (within an ulp); on gfx950 this equals the IEEE
+// reciprocal for every significand at every exponent of that range.
+__device__ __forceinline__ float rcp_rn(float d) {
+    const float y0 = __builtin_amdgcn_rcpf(d);
+    return __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
+}
+
 struct Div {
     float s, inv;
     bool fast;
     __device__ __forceinline__ void set(float s_) {
         s = s_;
-        inv = 1.0f / s_;
         fast = (s_ >= 0x1p-120f) && (s_ <= 0x1p120f);
+        inv = rcp_rn(s_);
+        if (!fast) inv = 1.0f / s_;
     }
     __device__ __forceinline__ float operator()(float x) const {
         if (fast) {
@@ -158,9 +174,10 @@ __device__ __forceinline__ Elem quant_elem(float x, const Div& d, float qmin, fl
 }
 
 // quant_elem for a scale known to be in the normal range [2^-120, 2^120]:
-// no zero case and the corrected division only, so no branches
+// no zero case and the corrected division only, so no branches; the grid
+// value is left to the caller
 template <int KIND>
-__device__ __forceinline__ Elem quant_fast(float x, const Div& d, float qmin, float qmax) {
+__device__ __forceinline__ Elem quant_fast_r(float x, const Div& d, float qmin, float qmax) {
     const float q0 = x * d.inv;
     const float rem = __builtin_fmaf(-q0, d.s, x);
     const float r = __builtin_fmaf(rem, d.inv, q0);
@@ -168,8 +185,26 @@ __device__ __forceinline__ Elem quant_fast(float x, const Div& d, float qmin, fl
     e.r = r;
     // NVFP4 and FP8 grids are symmetric (qmin = -qmax)
     e.inside = KIND == K_INT ? (r >= qmin) && (r <= qmax) : fabsf(r) <= qmax;
-    e.q = grid_q<KIND>(r, x, qmin, qmax);
     return e;
+}
+
+// grid values of two divided elements (signs from x), one conversion pair
+template <int KIND>
+__device__ __forceinline__ void grid_q2(Elem& e0, Elem& e1, float x0, float x1, float qmin, float qmax) {
+    if (KIND == K_NVFP4) {
+        float q0, q1;
+        e2m1_round2(fminf(fabsf(e0.r), 6.0f), fminf(fabsf(e1.r), 6.0f), &q0, &q1);
+        e0.q = copysignf(q0, x0);
+        e1.q = copysignf(q1, x1);
+    } else if (KIND == K_FP8) {
+        float q0, q1;
+        e4m3_round2(fminf(fabsf(e0.r), 448.0f), fminf(fabsf(e1.r), 448.0f), &q0, &q1);
+        e0.q = copysignf(q0, x0);
+        e1.q = copysignf(q1, x1);
+    } else {
+        e0.q = grid_q<KIND>(e0.r, x0, qmin, qmax);
+        e1.q = grid_q<KIND>(e1.r, x1, qmin, qmax);
+    }
 }
 
 // Run f(i, Elem) over the N elements x[0..N) sharing the effective scale s.
@@ -177,11 +212,17 @@ __device__ __forceinline__ Elem quant_fast(float x, const Div& d, float qmin, fl
 // the normal range (a wave-uniform branch), else the general one.
 template <int KIND, int N, typename F>
 __device__ __forceinline__ void quant_group(const float* x, float s, float qmin, float qmax, F&& f) {
+    static_assert(N % 2 == 0, "elements come in pairs");
     Div dv;
     dv.set(s);
     if (__all(dv.fast)) {
+        Elem e[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) f(i, quant_fast<KIND>(x[i], dv, qmin, qmax));
+        for (int i = 0; i < N; ++i) e[i] = quant_fast_r<KIND>(x[i], dv, qmin, qmax);
+#pragma unroll
+        for (int i = 0; i < N; i += 2) grid_q2<KIND>(e[i], e[i + 1], x[i], x[i + 1], qmin, qmax);
+#pragma unroll
+        for (int i = 0; i < N; ++i) f(i, e[i]);
     } else {
 #pragma unroll
         for (int i = 0; i < N; ++i) f(i, quant_elem<KIND>(x[i], dv, qmin, qmax));

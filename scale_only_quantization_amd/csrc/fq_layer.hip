@@ -386,14 +386,6 @@ __device__ __forceinline__ float exp2_taylor(float y) {
     return ldexpf(p, (int)n);
 }
 
-// 1/d correctly rounded for d in [2^-120, 2^120]: one Newton step with FMAs
-// from the hardware reciprocal (within an ulp); on gfx950 this equals the IEEE
-// reciprocal for every significand at every exponent of that range.
-__device__ __forceinline__ float rcp_rn(float d) {
-    const float y0 = __builtin_amdgcn_rcpf(d);
-    return __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
-}
-
 // silu(g) and sigmoid(g), as the forward and the backward both form them,
 // without branches and without overflow: with e = e^-|g| in [0, 1] and
 // den = 1 + e in [1, 2],
