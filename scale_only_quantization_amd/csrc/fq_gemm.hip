@@ -49,6 +49,9 @@
 #ifndef GEMM_PP
 #define GEMM_PP 1           // ping-pong schedule of the 8-wave tile (FWD, DGRAD)
 #endif
+#ifndef GEMM_PP_WG
+#define GEMM_PP_WG 0        // the same for WGRAD
+#endif
 
 namespace fq {
 
@@ -218,14 +221,50 @@ __device__ __forceinline__ int xcd_tile(int id, int grid, int tiles) {
     return (id / 8 < chunk && t < tiles) ? t : -1;
 }
 
-// sum of g c over 8 elements sharing the effective scale s
+// sum of g c over 8 elements sharing the effective scale s.  On the fast
+// path (every lane's scale normal) the NVFP4 grid value is converted from the
+// signed, clamped quotient directly: c = q - r only needs q's value, and a
+// zero element has c = 0 whatever the sign of its q.
 template <int KIND>
 __device__ __forceinline__ float sg_part8(const float* w8, const float* g8, float s, float qmin, float qmax) {
     float part = 0.0f;
+    if (KIND == K_NVFP4) {
+        Div dv;
+        dv.set(s);
+        if (__all(dv.fast)) {
+            float r[8], q[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const float q0 = w8[v] * dv.inv;
+                r[v] = __builtin_fmaf(__builtin_fmaf(-q0, dv.s, w8[v]), dv.inv, q0);
+            }
+#pragma unroll
+            for (int v = 0; v < 8; v += 2)
+                e2m1_round2(__builtin_amdgcn_fmed3f(r[v], -6.0f, 6.0f), __builtin_amdgcn_fmed3f(r[v + 1], -6.0f, 6.0f),
+                            &q[v], &q[v + 1]);
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const float c = q[v] - (fabsf(r[v]) <= 6.0f ? r[v] : 0.0f);
+                part = __builtin_fmaf(g8[v], c, part);
+            }
+            return part;
+        }
+    }
     quant_group<KIND, 8>(w8, s, qmin, qmax, [&](int v, const Elem& el) {
         part = __builtin_fmaf(g8[v], ste_c(el, qmin, qmax), part);
     });
     return part;
+}
+
+// fl32(s / t) for the NVFP4 block factor: Markstein's corrected quotient from
+// inv_t = RN(1/t) when t is normal (the caller's wave-uniform tfast), IEEE
+// division otherwise
+__device__ __forceinline__ float div_by_t(float s, float t, float inv_t, bool tfast) {
+    if (tfast) {
+        const float q0 = s * inv_t;
+        return __builtin_fmaf(__builtin_fmaf(-q0, t, s), inv_t, q0);
+    }
+    return s / t;
 }
 
 // Weight-gradient epilogue with the weight-scale gradient fused: the wave's
@@ -354,6 +393,8 @@ __device__ __forceinline__ void sg_epilogue_lds(const GemmArgs& g, const f32x16 
     const float qmin = sg.q.qmin, qmax = sg.q.qmax;
     const int gran = sg.q.gran, group = sg.q.group;
     const float t = KIND == K_NVFP4 ? sg.tscale[e] : 0.0f;
+    const bool tfast = t >= 0x1p-120f && t <= 0x1p120f;      // t is one per expert: wave-uniform
+    const float inv_t = KIND == K_NVFP4 ? rcp_rn(t) : 0.0f;
     float sv[WTM][WTN][2];
     // scales of slice ti (the loads' waits are the compiler's): the row's four
     // 16-column blocks are one 16-B load when each block has its own scale
@@ -408,7 +449,7 @@ __device__ __forceinline__ void sg_epilogue_lds(const GemmArgs& g, const f32x16 
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 float sc = sv[ti][tj][b];
-                if (KIND == K_NVFP4) sc = t * e4m3_round(fminf(sc / t, 448.0f));
+                if (KIND == K_NVFP4) sc = t * e4m3_round(fminf(div_by_t(sc, t, inv_t, tfast), 448.0f));
                 const uint2 wa = wv[tj][2 * b], wb = wv[tj][2 * b + 1];
                 const float w8[8] = {bf_lo(wa.x), bf_hi(wa.x), bf_lo(wa.y), bf_hi(wa.y),
                                      bf_lo(wb.x), bf_hi(wb.x), bf_lo(wb.y), bf_hi(wb.y)};
@@ -559,7 +600,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
     // (the weight gradient keeps the single-phase loop: with both operands
     // read transposed its memory phase outlasts a compute phase; measured
     // 7-12% slower)
-    constexpr bool PP = GEMM_PP && NW == 8 && S == 2 && WVM == 2 && MODE != WGRAD;
+    constexpr bool PP = GEMM_PP && NW == 8 && S == 2 && WVM == 2 && (MODE != WGRAD || GEMM_PP_WG);
     auto mainloop_pp = [&](int nk, bool pre0) {
         const int grp = wave_id() >> 2;
         bf16x8 af[KS][WTM], bfr[KS][WTN];
@@ -676,15 +717,26 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         }
         __syncthreads();
         constexpr int RPI = 64 / CH;                             // rows per wave instruction
+        constexpr int NIT = BM / (RPI * NW);                     // store instructions per wave
+        // every row segment of this wave from LDS first (one wait), then the
+        // stores through a resource bounded to the tile's expert rows, so the
+        // rows past m_end are dropped without branches; non-temporal (the
+        // output is next read by another kernel)
+        u32x4 cv[NIT];
 #pragma unroll
-        for (int it = 0; it < BM / (RPI * NW); ++it) {
+        for (int it = 0; it < NIT; ++it) {
             const int row = (it * NW + wave) * RPI + lane / CH;
             const int c = lane % CH;
-            const int64_t r = m0 + row;
-            const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            cv[it] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
                 smem + row * RB + ((c ^ (row & 15)) << 4));
-            // streaming (non-temporal) stores: the output is next read by another kernel
-            if (r < m_end) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.C) + r * g.ldc + n0 + c * 8));
+        }
+        const __amdgpu_buffer_rsrc_t crs =
+            make_rsrc(static_cast<uint16_t*>(g.C) + m0 * g.ldc + n0, (m_end - m0 - 1) * g.ldc * 2 + BN * 2);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int row = (it * NW + wave) * RPI + lane / CH;
+            const int c = lane % CH;
+            __builtin_amdgcn_raw_buffer_store_b128(cv[it], crs, (uint32_t)(row * g.ldc * 2 + c * 16), 0, 2);
         }
     } else {
         // Persistent: the blocks of XCD group x = blockIdx % 8 (dealt to XCD x)
@@ -774,6 +826,8 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             }
             if (!more) break;
         }
+        // nothing direct-to-LDS may be in flight when the block's LDS is released
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 }
 
