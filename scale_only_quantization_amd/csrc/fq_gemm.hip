@@ -21,11 +21,14 @@
 //   K-contiguous operand: LDS [rows][BK], the 16-B chunk index XORed with a
 //     row swizzle; a fragment (8 consecutive k of one row) is one
 //     ds_read_b128, and the 16 rows of one read pass fall on distinct banks.
-//   Row-contiguous operand: LDS [BK][rows] as in memory, the 16-B chunk index
-//     XOR 4 (k & 3), so the 32 lanes of one ds_read_b64_tr_b16 pass (4 k-rows
-//     x 64 B) fall on distinct banks; a fragment is two such reads: inside each group
-//     of 16 lanes, lane i points at k-row kb + i/4, columns mb + 4(i%4) .. +3,
-//     and lane j receives k = kb .. kb+3 of column mb + j.
+//   Row-contiguous operand: LDS [BK][rows] as in memory, 16-B chunk c of k-row
+//     k stored at chunk c ^ 2 (k & 3) ^ 8 (bit 1 of c); a fragment is two
+//     ds_read_b64_tr_b16: inside each group of 16 lanes, lane i points at
+//     k-row kb + i/4, columns mb + 4(i%4) .. +3, and lane j receives
+//     k = kb .. kb+3 of column mb + j.  The swizzle spreads a group's 4 rows
+//     over 8 chunks and puts the two groups of one 32-column half on opposite
+//     halves of the banks: these reads then run at 140 B/clk per CU, against
+//     107 with chunk c ^ 4 (k & 3) and 58 unswizzled (measured on gfx950).
 // FWD/DGRAD row tiles come from a device-side tile table (expert, first row)
 // built by the routing scan, so no host read-back of the counts is needed.
 // WGRAD is persistent: each XCD works through its own experts' tiles (an
@@ -36,8 +39,12 @@
 #include "fq_internal.h"
 
 #ifndef GEMM_BK_BIG
-#define GEMM_BK_BIG 64
+#define GEMM_BK_BIG 64      // reduction step and LDS stages of the large FWD/DGRAD tile
 #define GEMM_S_BIG 2
+#endif
+#ifndef GEMM_BK_WG
+#define GEMM_BK_WG 64       // the same for the large WGRAD tile
+#define GEMM_S_WG 2
 #endif
 #ifndef GEMM_XCD
 #define GEMM_XCD 1          // contiguous tile runs per XCD for FWD/DGRAD
@@ -75,6 +82,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Wait until at most n (clamped to 0..3) steps of L load instructions each
+// are outstanding: vector-memory loads complete in issue order.
+template <int L>
+__device__ __forceinline__ void wait_steps(int n) {
+    static_assert(3 * L <= 63, "vmcnt range");
+    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L) : "memory");
+}
 
 // K-contiguous operand tile [ROWS][BK]: element (row, k) at byte row*ld2 + 2k
 // of the resource.  Rows of 2 BK bytes; each 1-KB wave load covers 512/BK rows.
@@ -145,8 +163,10 @@ struct MNTile {
     static constexpr int BYTES = ROWS * BK * 2;
     static constexpr int PER_WAVE = BYTES / 1024 / NW;
     static constexpr int RB = ROWS * 2;               // bytes per k-row
+    // 16-B chunk ch of k-row k is stored at chunk ch ^ 2 (k & 3) ^ 8 (bit 1 of ch)
+    __device__ static __forceinline__ int phys(int k, int ch) { return ch ^ ((k & 3) << 1) ^ (((ch >> 1) & 1) << 3); }
     __device__ static __forceinline__ int off(int k, int byte) {   // swizzled byte offset
-        return k * RB + (((byte >> 4) ^ ((k & 3) << 2)) << 4) + (byte & 15);
+        return k * RB + (phys(k, byte >> 4) << 4) + (byte & 15);
     }
     __amdgpu_buffer_rsrc_t rs;
     uint32_t voff[PER_WAVE];
@@ -160,7 +180,7 @@ struct MNTile {
             const int pos = (NW * i + w) * 1024 + lane * 16;  // byte position in the tile
             const int k = pos / RB;
             const int pc = (pos % RB) >> 4;
-            const int lc = pc ^ ((k & 3) << 2);
+            const int lc = pc ^ ((k & 3) << 1) ^ ((((pc >> 1) ^ k) & 1) << 3);   // phys(k, lc) == pc
             voff[i] = (uint32_t)(k * ld * 2 + lc * 16);
         }
     }
@@ -380,25 +400,23 @@ struct WStage {
     }
 };
 
-// The epilogue above with the weights read from the wave's LDS slots: slices
-// 0 and 1 were issued before the call; slice ti + 2 refills slice ti's slot as
-// soon as slice ti's weights are in registers.  A wait on the vector memory
-// counter also covers the direct-to-LDS loads; this wave alone reads its slots.
+// The epilogue above with the weights read from the wave's LDS slots, in two
+// parts.  begin(): the scales of slices 0 and 1 (issued, like slices 0 and 1
+// of the weights, before the next tile's first loads).  run(): waits until at
+// most `later` steps of L loads (the next tile's) are outstanding, then
+// reduces slice by slice; slice ti + 2 refills slice ti's slot as soon as
+// slice ti's weights are in registers.  A wait on the vector memory counter
+// also covers the direct-to-LDS loads; this wave alone reads its slots.
 template <int KIND, int WTM, int WTN>
-__device__ __forceinline__ void sg_epilogue_lds(const GemmArgs& g, const f32x16 (&acc)[WTM][WTN], int e,
-                                                int i_w, int j_w, int lane, const WStage& ws, lds_t* slots) {
+struct SgEpiLds {
     static_assert(WTN == 2 && WTM >= 2, "two 32-column tiles per wave, two slots");
-    const SgArgs& sg = g.sg;
-    const int64_t N = g.N, K = g.K;
-    const float qmin = sg.q.qmin, qmax = sg.q.qmax;
-    const int gran = sg.q.gran, group = sg.q.group;
-    const float t = KIND == K_NVFP4 ? sg.tscale[e] : 0.0f;
-    const bool tfast = t >= 0x1p-120f && t <= 0x1p120f;      // t is one per expert: wave-uniform
-    const float inv_t = KIND == K_NVFP4 ? rcp_rn(t) : 0.0f;
     float sv[WTM][WTN][2];
     // scales of slice ti (the loads' waits are the compiler's): the row's four
     // 16-column blocks are one 16-B load when each block has its own scale
-    auto load_sv = [&](int ti) {
+    __device__ __forceinline__ void load_sv(const GemmArgs& g, int e, int i_w, int j_w, int lane, int ti) {
+        const SgArgs& sg = g.sg;
+        const int64_t N = g.N, K = g.K;
+        const int gran = sg.q.gran, group = sg.q.group;
         const int64_t wrow = (int64_t)e * N + i_w + ti * 32 + (lane & 31);
         if (KIND == K_NVFP4 || (gran == G_GROUP && group == 16)) {
             typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
@@ -422,56 +440,68 @@ __device__ __forceinline__ void sg_epilogue_lds(const GemmArgs& g, const f32x16 
                 const int j = j_w + tj * 32 + 16 * b;
                 sv[ti][tj][b] = sg.scale[wrow * (K / group) + j / group];
             }
-    };
-    load_sv(0);
-    load_sv(1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __device__ __forceinline__ void begin(const GemmArgs& g, int e, int i_w, int j_w, int lane) {
+        load_sv(g, e, i_w, j_w, lane, 0);
+        load_sv(g, e, i_w, j_w, lane, 1);
+    }
+    template <int L>
+    __device__ __forceinline__ void run(const GemmArgs& g, const f32x16 (&acc)[WTM][WTN], int e, int i_w, int j_w,
+                                        int lane, const WStage& ws, lds_t* slots, int later) {
+        const SgArgs& sg = g.sg;
+        const int64_t N = g.N, K = g.K;
+        const float qmin = sg.q.qmin, qmax = sg.q.qmax;
+        const float t = KIND == K_NVFP4 ? sg.tscale[e] : 0.0f;
+        const bool tfast = t >= 0x1p-120f && t <= 0x1p120f;      // t is one per expert: wave-uniform
+        const float inv_t = KIND == K_NVFP4 ? rcp_rn(t) : 0.0f;
+        wait_steps<L>(later);
 #pragma unroll
-    for (int ti = 0; ti < WTM; ++ti) {
-        lds_t* slot = slots + (ti & 1) * 4096;
-        if (ti == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slices 2 and 3 have landed
-        const int64_t wrow = (int64_t)e * N + i_w + ti * 32 + (lane & 31);
-        uint2 wv[WTN][4];
+        for (int ti = 0; ti < WTM; ++ti) {
+            lds_t* slot = slots + (ti & 1) * 4096;
+            if (ti == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slices 2 and 3 have landed
+            const int64_t wrow = (int64_t)e * N + i_w + ti * 32 + (lane & 31);
+            uint2 wv[WTN][4];
 #pragma unroll
-        for (int tj = 0; tj < WTN; ++tj)
+            for (int tj = 0; tj < WTN; ++tj)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) wv[tj][q] = WStage::read(slot, 4 * tj + q);
-        if (ti + 2 < WTM) {
-            load_sv(ti + 2);
-            // the slot's reads have returned before it is refilled
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            ws.issue(slot, ti + 2);
-        }
-#pragma unroll
-        for (int tj = 0; tj < WTN; ++tj) {
-            const int jt = j_w + tj * 32;
-            float p[2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                float sc = sv[ti][tj][b];
-                if (KIND == K_NVFP4) sc = t * e4m3_round(fminf(div_by_t(sc, t, inv_t, tfast), 448.0f));
-                const uint2 wa = wv[tj][2 * b], wb = wv[tj][2 * b + 1];
-                const float w8[8] = {bf_lo(wa.x), bf_hi(wa.x), bf_lo(wa.y), bf_hi(wa.y),
-                                     bf_lo(wb.x), bf_hi(wb.x), bf_lo(wb.y), bf_hi(wb.y)};
-                float g8[8];
-#pragma unroll
-                for (int v = 0; v < 8; ++v) g8[v] = acc[ti][tj][8 * b + v];
-                p[b] = sg_part8<KIND>(w8, g8, sc, qmin, qmax);
+                for (int q = 0; q < 4; ++q) wv[tj][q] = WStage::read(slot, 4 * tj + q);
+            if (ti + 2 < WTM) {
+                load_sv(g, e, i_w, j_w, lane, ti + 2);
+                // the slot's reads have returned before it is refilled
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                ws.issue(slot, ti + 2);
             }
-            const float b0 = p[0] + __shfl_xor(p[0], 32);
-            const float b1 = p[1] + __shfl_xor(p[1], 32);
-            if (lane < 32) {
-                if (!sg.part32) {
-                    float* o = sg.out + wrow * (K >> 4) + (jt >> 4);
-                    o[0] = b0;
-                    o[1] = b1;
-                } else {
-                    sg.out[wrow * (K >> 5) + (jt >> 5)] = b0 + b1;
+#pragma unroll
+            for (int tj = 0; tj < WTN; ++tj) {
+                const int jt = j_w + tj * 32;
+                float p[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    float sc = sv[ti][tj][b];
+                    if (KIND == K_NVFP4) sc = t * e4m3_round(fminf(div_by_t(sc, t, inv_t, tfast), 448.0f));
+                    const uint2 wa = wv[tj][2 * b], wb = wv[tj][2 * b + 1];
+                    const float w8[8] = {bf_lo(wa.x), bf_hi(wa.x), bf_lo(wa.y), bf_hi(wa.y),
+                                         bf_lo(wb.x), bf_hi(wb.x), bf_lo(wb.y), bf_hi(wb.y)};
+                    float g8[8];
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) g8[v] = acc[ti][tj][8 * b + v];
+                    p[b] = sg_part8<KIND>(w8, g8, sc, qmin, qmax);
+                }
+                const float b0 = p[0] + __shfl_xor(p[0], 32);
+                const float b1 = p[1] + __shfl_xor(p[1], 32);
+                if (lane < 32) {
+                    if (!sg.part32) {
+                        float* o = sg.out + wrow * (K >> 4) + (jt >> 4);
+                        o[0] = b0;
+                        o[1] = b1;
+                    } else {
+                        sg.out[wrow * (K >> 5) + (jt >> 5)] = b0 + b1;
+                    }
                 }
             }
         }
     }
-}
+};
 
 template <int MODE, int WVM, int WVN, int WTM, int WTN, int BK, int S>
 __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmArgs g) {
@@ -551,57 +581,63 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         la.issue(stage_a(kt), kt * BK);
         lb.issue(stage_b(kt), kt * BK);
     };
-    // the first S-1 steps in flight
-    auto prologue = [&](int nk) {
+    // steps [p0, p1] of this wave's loads (those below nk)
+    auto issue_steps = [&](int nk, int p0, int p1) {
 #pragma unroll
-        for (int p = 0; p < S - 1; ++p)
-            if (p < nk) issue(p);
+        for (int p = 0; p < S; ++p)
+            if (p >= p0 && p <= p1 && p < nk) issue(p);
     };
-    auto mainloop = [&](int nk) {
+    // Single-phase loop: every wave waits for step kt, one barrier, then the
+    // loads of step kt+S-1 and the MFMAs of step kt.  pre: steps [0, pre)
+    // were issued before the call (into stages the caller may have used
+    // since, hence the barrier before the rest of the prologue).
+    // first(): called once, after the first step's loads are issued (memory
+    // operations it starts overlap the first step)
+    auto mainloop = [&](int nk, int pre, auto&& first) {
         fa.prep(wm * 32 * WTM);
         fb.prep(wn * 32 * WTN);
+        if (pre > 0) __syncthreads();
+        issue_steps(nk, pre, S - 2);
+        if (nk <= 0) first();
         for (int kt = 0; kt < nk; ++kt) {
-            // this wave's loads of step kt are done once at most the loads of the
-            // S-2 later steps are outstanding; the barrier then covers every wave
-            if (kt + S - 2 < nk) {
-                if constexpr (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                else if constexpr (S == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-                else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
-            } else {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            }
+            // this wave's loads of step kt are done once at most those of the
+            // later steps already issued are outstanding; the barrier then
+            // covers every wave
+            wait_steps<LOADS>(min(S - 2, nk - 1 - kt));
             __syncthreads();
             // the stage step kt+S-1 overwrites was read in step kt-1, finished by every wave
             if (kt + S - 1 < nk) issue(kt + S - 1);
+            if (kt == 0) first();
             compute(kt);
         }
     };
 
-    // Ping-pong schedule of the 8-wave tile with 2 LDS stages.  Waves 0-3
-    // (group 0) and 4-7 (group 1), one of each per SIMD, alternate between a
-    // memory phase (every fragment of one BK step read from LDS into
-    // registers, and this wave's global loads) and a compute phase (that
-    // step's MFMAs from registers), group 1 one phase behind.  Between two
-    // barriers one wave on each SIMD issues MFMAs while the other reads LDS and
-    // waits on memory, so the matrix core does not idle across the barrier and
-    // the fragment reads that follow it.
-    //   group 0, memory phase of step kt: its loads of step kt+1 (into the
-    //     stage step kt-1 used, read by both groups in the two phases before),
-    //     then its fragment reads of step kt; it waits for those loads after
-    //     its next compute phase.
+    // Ping-pong schedule of the 8-wave tile.  Waves 0-3 (group 0) and 4-7
+    // (group 1), one of each per SIMD, alternate between a memory phase
+    // (every fragment of one BK step read from LDS into registers, and this
+    // wave's global loads) and a compute phase (that step's MFMAs from
+    // registers), group 1 one phase behind.  Between two barriers one wave on
+    // each SIMD issues MFMAs while the other reads LDS and waits on memory, so
+    // the matrix core does not idle across the barrier and the fragment reads
+    // that follow it.
+    //   group 0, memory phase of step kt: its loads of step kt+S-1 (into the
+    //     stage step kt-1 used, read by both groups in the two phases
+    //     before), then its fragment reads of step kt; it waits for its loads
+    //     of step kt+1 after its next compute phase.
     //   group 1, memory phase of step kt: its fragment reads of step kt, then
-    //     (once they have returned) its loads of step kt+2 into the same stage
+    //     (once they have returned) its loads of step kt+S into the same stage
     //     (group 0 read it one phase earlier), then it waits for its loads of
     //     step kt+1.
     // Every load of step kt+1 has landed before the barrier that opens group
-    // 0's memory phase of step kt+1.  pre0: every wave's loads of step 0 were
-    // issued before the call (and LDS stage 1 may still be in use until the
-    // first barrier).
-    // (the weight gradient keeps the single-phase loop: with both operands
-    // read transposed its memory phase outlasts a compute phase; measured
-    // 7-12% slower)
-    constexpr bool PP = GEMM_PP && NW == 8 && S == 2 && WVM == 2 && (MODE != WGRAD || GEMM_PP_WG);
-    auto mainloop_pp = [&](int nk, bool pre0) {
+    // 0's memory phase of step kt+1.  Prologue: group 0 has steps [0, S-2] in
+    // flight, group 1 steps [0, S-1]; pre: steps [0, pre) were issued by every
+    // wave before the call.
+    // (with 64-deep steps and two stages the weight gradient keeps the
+    // single-phase loop: with both operands read transposed its memory phase
+    // outlasts a compute phase and the step's fragments spill; measured 7-12%
+    // slower)
+    constexpr bool PP = GEMM_PP && NW == 8 && WVM == 2 && (MODE != WGRAD || GEMM_PP_WG);
+    auto mainloop_pp = [&](int nk, int pre, auto&& first) {
         const int grp = wave_id() >> 2;
         bf16x8 af[KS][WTM], bfr[KS][WTN];
         fa.prep(wm * 32 * WTM);
@@ -611,26 +647,17 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         };
-        if (!pre0) {
-            issue(0);
-            if (grp == 1 && nk > 1) {
-                issue(1);
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-            } else {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            }
-            bar();
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            bar();
-            if (grp == 1 && nk > 1) issue(1);
-        }
+        if (pre > 0) bar();
+        const int last = grp == 0 ? S - 2 : S - 1;
+        issue_steps(nk, pre, last);
+        wait_steps<LOADS>(min(last, nk - 1));
+        bar();
         if (grp == 1) bar();
         auto phases = [&](int kt, int st) {
             // memory phase
-            if (grp == 0 && kt + 1 < nk) issue(kt + 1);
+            if (grp == 0 && kt + S - 1 < nk) issue(kt + S - 1);
             const lds_t* sa = smem + st * A_BYTES;
-            const lds_t* sb = smem + 2 * A_BYTES + st * B_BYTES;
+            const lds_t* sb = smem + S * A_BYTES + st * B_BYTES;
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
@@ -640,12 +667,8 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (grp == 1) {
-                if (kt + 2 < nk) {
-                    issue(kt + 2);
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-                } else {
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                }
+                if (kt + S < nk) issue(kt + S);
+                wait_steps<LOADS>(min(S - 1, nk - 2 - kt));
             }
             bar();
             // compute phase
@@ -657,15 +680,18 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
                     for (int tj = 0; tj < WTN; ++tj)
                         acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][tj], af[kk][ti], acc[ti][tj],
                                                                               0, 0, 0);
-            if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (grp == 0) wait_steps<LOADS>(min(S - 2, nk - 2 - kt));
             bar();
         };
-        for (int kt = 0; kt < nk; kt += 2) {
-            phases(kt, 0);
-            if (kt + 1 < nk) phases(kt + 1, 1);
+        first();
+        for (int kt = 0; kt < nk; kt += S) {
+#pragma unroll
+            for (int u = 0; u < S; ++u)
+                if (kt + u < nk) phases(kt + u, u);
         }
         if (grp == 0) bar();
     };
+    auto no_hook = []() {};
 
     if constexpr (MODE != WGRAD) {
         const int ntn = g.N / BN;
@@ -686,12 +712,8 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         else
             lb.init(make_rsrc(Be + n0, ((int64_t)g.K - 1) * g.ldb * 2 + (int64_t)BN * 2), g.ldb);
         zero_acc();
-        if constexpr (PP) {
-            mainloop_pp(nk, false);
-        } else {
-            prologue(nk);
-            mainloop(nk);
-        }
+        if constexpr (PP) mainloop_pp(nk, 0, no_hook);
+        else mainloop(nk, 0, no_hook);
         // Epilogue through LDS, so that global stores are whole row segments:
         // lane holds C[m = lane%32][n = 8*(v/4) + 4*(lane/32) + v%4] of each
         // 32x32 tile; it is written as bf16 into an LDS tile [BM][BN] whose
@@ -743,7 +765,11 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         // take the tiles of that XCD's experts (longest first) from a counter,
         // so the tiles sharing an expert's operand rows meet in one L2.  The
         // next tile's first loads are issued before this tile's epilogue.
-        __shared__ int s_slot;
+        // Slots are taken one tile ahead: tile t's epilogue takes the slot of
+        // tile t + 2 into s_q[t & 1], read after tile t + 1's main loop (main
+        // loop barriers separate each write from the reads around it), so the
+        // atomic's round trip hides behind the epilogue's own loads.
+        __shared__ int s_slot, s_q[2];
         const int x = blockIdx.x & 7;
         const int tj_n = g.K / BN;                     // output [N, K] per expert
         const int tpe = (g.N / BM) * tj_n;
@@ -762,46 +788,59 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             la.init(make_rsrc(g.A + rb * g.lda + i0, (int64_t)me * g.lda * 2 - i0 * 2), g.lda);
             lb.init(make_rsrc(g.B + rb * g.ldb + n0, (int64_t)me * g.ldb * 2 - n0 * 2), g.ldb);
         };
-        if (threadIdx.x == 0) s_slot = atomicAdd(g.wg_ctr + x, 1);
+        if (threadIdx.x == 0) {
+            s_slot = atomicAdd(g.wg_ctr + x, 1);
+            s_q[1] = atomicAdd(g.wg_ctr + x, 1);       // tile 1's slot, read after tile 0's main loop
+        }
         __syncthreads();
-        int slot = s_slot;
+        const int slot = s_slot;
         if (slot < 0 || slot >= tiles_x) return;
+        // The next tile's first PRE steps are issued before this tile's
+        // epilogue, into stages [0, PRE); the fused epilogue's weights go
+        // through the stages after them (of A for waves 0-3, of B for waves
+        // 4-7), two 4-KB slots per wave.
+        // (without that epilogue the whole prologue, S-1 steps)
+        constexpr int SLOT_STAGES = (4 * 8192 + A_BYTES - 1) / A_BYTES;
+        constexpr bool LDS_EPI = WTN == 2 && WTM >= 2 && NW == 8 && S > SLOT_STAGES && A_BYTES == B_BYTES;
+        constexpr int PRE = LDS_EPI ? S - SLOT_STAGES : S - 1;
         setup(slot);
-        prologue(nk);
-        // the fused epilogue's weights go through the stage the next tile's
-        // first loads leave free (stage 1 of A for waves 0-3, of B for waves
-        // 4-7), two 4-KB slots per wave
-        constexpr bool LDS_EPI = S == 2 && WTN == 2 && WTM >= 2 && NW == 8 && A_BYTES >= 4 * 8192 &&
-                                 B_BYTES >= 4 * 8192;
+        issue_steps(nk, 0, PRE - 1);
         const int wu = wave_id();                     // wave-uniform: LDS base and resource
-        lds_t* wslots = wu < 4 ? smem + A_BYTES + wu * 8192 : smem + 2 * A_BYTES + B_BYTES + (wu - 4) * 8192;
+        lds_t* wslots = wu < 4 ? smem + PRE * A_BYTES + wu * 8192
+                               : smem + S * A_BYTES + PRE * B_BYTES + (wu - 4) * 8192;
         WStage ws;
-        for (;;) {
+        for (int tcount = 0;; ++tcount) {
             zero_acc();
-            if constexpr (PP) mainloop_pp(nk, true);
-            else mainloop(nk);
-            __syncthreads();          // LDS stages free; every wave has read s_slot
+            if constexpr (PP) mainloop_pp(nk, PRE, no_hook);
+            else mainloop(nk, PRE, no_hook);
+            __syncthreads();          // LDS stages free; s_q[(tcount - 1) & 1] written before the main loop
+            const int next = s_q[(tcount - 1) & 1];
+            const bool more = next >= 0 && next < tiles_x;
+            int after = 0;
+            if (threadIdx.x == 0 && more) after = atomicAdd(g.wg_ctr + x, 1);
             if (LDS_EPI && g.sg.out) {
                 ws.init(g.sg.W + ((int64_t)e * g.N + i0 + (wu / WVN) * 32 * WTM) * g.K + n0 + (wu % WVN) * 32 * WTN,
                         g.K, 32 * WTM);
                 ws.issue(wslots, 0);
                 ws.issue(wslots + 4096, 1);
             }
-            if (threadIdx.x == 0) s_slot = atomicAdd(g.wg_ctr + x, 1);
-            __syncthreads();
-            const int next = s_slot;
             const int ce = e, ci0 = i0, cn0 = n0;
-            const bool more = next >= 0 && next < tiles_x;
             if (more) {
                 setup(next);
-                prologue(nk);
+                issue_steps(nk, 0, PRE - 1);
             }
             if (g.sg.out) {
                 const int iw = ci0 + wm * 32 * WTM, jw = cn0 + wn * 32 * WTN;
+                auto lds_epi = [&](auto kind_c) {
+                    constexpr int KIND = decltype(kind_c)::value;
+                    SgEpiLds<KIND, WTM, WTN> ep;
+                    ep.begin(g, ce, iw, jw, lane);
+                    ep.template run<LOADS>(g, acc, ce, iw, jw, lane, ws, wslots, 0);
+                };
                 if constexpr (LDS_EPI) {
-                    if (g.sg.q.kind == K_NVFP4) sg_epilogue_lds<K_NVFP4, WTM, WTN>(g, acc, ce, iw, jw, lane, ws, wslots);
-                    else if (g.sg.q.kind == K_INT) sg_epilogue_lds<K_INT, WTM, WTN>(g, acc, ce, iw, jw, lane, ws, wslots);
-                    else sg_epilogue_lds<K_FP8, WTM, WTN>(g, acc, ce, iw, jw, lane, ws, wslots);
+                    if (g.sg.q.kind == K_NVFP4) lds_epi(std::integral_constant<int, K_NVFP4>{});
+                    else if (g.sg.q.kind == K_INT) lds_epi(std::integral_constant<int, K_INT>{});
+                    else lds_epi(std::integral_constant<int, K_FP8>{});
                 } else {
                     if (g.sg.q.kind == K_NVFP4) sg_epilogue<K_NVFP4, WTM, WTN>(g, acc, ce, iw, jw, lane);
                     else if (g.sg.q.kind == K_INT) sg_epilogue<K_INT, WTM, WTN>(g, acc, ce, iw, jw, lane);
@@ -824,6 +863,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
                     }
                 }
             }
+            if (threadIdx.x == 0 && more) s_q[tcount & 1] = after;
             if (!more) break;
         }
         // nothing direct-to-LDS may be in flight when the block's LDS is released
@@ -834,6 +874,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
 // Large tile: 256 x 256 outputs, as WVM_BIG x WVN_BIG waves of
 // (256 / WVM_BIG) x (256 / WVN_BIG); small tile: 128 x 128, 2 x 2 waves.
 constexpr int BK_BIG = GEMM_BK_BIG, S_BIG = GEMM_S_BIG, BK_SMALL = 32, S_SMALL = 3;
+constexpr int BK_WG = GEMM_BK_WG, S_WG = GEMM_S_WG;
 constexpr int WVM_BIG = GEMM_WVM, WVN_BIG = GEMM_WVN;
 #ifdef GEMM_WTM
 constexpr int WTM_BIG = GEMM_WTM, WTN_BIG = GEMM_WTN;
@@ -842,7 +883,8 @@ constexpr int WTM_BIG = 8 / WVM_BIG, WTN_BIG = 8 / WVN_BIG;
 #endif
 constexpr int BM_BIG = 32 * WTM_BIG * WVM_BIG, BN_BIG = 32 * WTN_BIG * WVN_BIG;
 static_assert(BM_BIG == 256, "the large row tile is the 256-row tile table");
-#define FQ_BIG(MODE) k_gemm<MODE, WVM_BIG, WVN_BIG, WTM_BIG, WTN_BIG, BK_BIG, S_BIG>
+#define FQ_BIG(MODE) \
+    k_gemm<MODE, WVM_BIG, WVN_BIG, WTM_BIG, WTN_BIG, MODE == WGRAD ? BK_WG : BK_BIG, MODE == WGRAD ? S_WG : S_BIG>
 #define FQ_SMALL(MODE) k_gemm<MODE, 2, 2, 2, 2, BK_SMALL, S_SMALL>
 
 // Explicit instantiations: without them the host pass does not emit every

@@ -256,6 +256,8 @@ def _calibrate(q, W):
     a = np.abs(np.asarray(W, np.float32))
     E, N, K = a.shape
     mat = a.reshape(E, -1).max(1)
+    if q.source == "dynamic" and q.kind != "nvfp4":
+        return None, None                                              # scales from the data
     if q.kind == "nvfp4":
         return None, (mat / np.float32(2688)).astype(np.float32)       # dynamic blocks: t only
     top = np.float32(448.0 if q.kind == "fp8" else q.qmax)
@@ -278,6 +280,8 @@ WEIGHT_QUANTISERS = {
     "int4-g8": QSpec("int", "group", 8, "learnable", -8, 7),
     # NVFP4 with dynamic block factors: the learnable tensor scale, through a stored dW^
     "nvfp4-dynamic": QSpec("nvfp4", "group", 16, "dynamic"),
+    # dynamic per-row FP8: no trainable weight scale (no weight-gradient GEMM)
+    "fp8-row-dynamic": QSpec("fp8", "row", 0, "dynamic"),
 }
 
 
