@@ -370,19 +370,19 @@ __global__ __launch_bounds__(TPB) void k_permute_a1(PermuteArgs a) {
 // (relative; results below 2^-126 within that plus (1 + |g|) 2^-149).
 // e^-|g| = 2^y, y = -|g| log2(e) clamped at -200 (2^-200 is 0 in fp32):
 // 2^y = 2^rint(y) * P(y - rint(y)), P the degree-7 Taylor polynomial of 2^f
-// (coefficients (ln 2)^i / i!, rounded to fp32), Horner with separate multiply
-// and add; the 2|g| term is the rounding of y.
+// (coefficients (ln 2)^i / i!, rounded to fp32), Horner with one fused
+// multiply-add per degree; the 2|g| term is the rounding of y.
 __device__ __forceinline__ float exp2_taylor(float y) {
     const float n = rintf(y);
     const float f = y - n;
     float p = 0x1.ffcbfcp-17f;
-    p = p * f; p = p + 0x1.430912p-13f;
-    p = p * f; p = p + 0x1.5d87fep-10f;
-    p = p * f; p = p + 0x1.3b2ab6p-7f;
-    p = p * f; p = p + 0x1.c6b08ep-5f;
-    p = p * f; p = p + 0x1.ebfbe0p-3f;
-    p = p * f; p = p + 0x1.62e430p-1f;
-    p = p * f; p = p + 1.0f;
+    p = __builtin_fmaf(p, f, 0x1.430912p-13f);
+    p = __builtin_fmaf(p, f, 0x1.5d87fep-10f);
+    p = __builtin_fmaf(p, f, 0x1.3b2ab6p-7f);
+    p = __builtin_fmaf(p, f, 0x1.c6b08ep-5f);
+    p = __builtin_fmaf(p, f, 0x1.ebfbe0p-3f);
+    p = __builtin_fmaf(p, f, 0x1.62e430p-1f);
+    p = __builtin_fmaf(p, f, 1.0f);
     return ldexpf(p, (int)n);
 }
 
@@ -392,8 +392,9 @@ __device__ __forceinline__ float exp2_taylor(float y) {
 //     g >= 0:  silu = g / den,      sigmoid = 1 / den
 //     g <  0:  silu = g e / den,    sigmoid = e / den
 // (both are g / (1 + e^-g)).  The quotient is Markstein's correction of
-// num RN(1/den) (the rounded quotient while it is normal); the sign is g's,
-// so silu(-0) = -0.
+// num RN(1/den) (the rounded quotient while it is normal): where e rounds
+// away (den = 1) silu is g exactly, as the exact value rounds; the sign is
+// g's, so silu(-0) = -0.
 __device__ __forceinline__ float silu_sig(float g, float* sig) {
     const float e = exp2_taylor(fmaxf(-fabsf(g) * 0x1.715476p+0f, -200.0f));
     const float den = 1.0f + e;
