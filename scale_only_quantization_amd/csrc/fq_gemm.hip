@@ -83,6 +83,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// x of lane l ^ 32: one cross-half swap (v_permlane32_swap) and a select, no
+// LDS round trip.  The swap returns (lanes 0-31 of x in both halves, lanes
+// 32-63 of x in both halves).
+__device__ __forceinline__ float xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // Wait until at most n (clamped to 0..3) steps of L load instructions each
 // are outstanding: vector-memory loads complete in issue order.
 template <int L>
@@ -349,8 +357,8 @@ __device__ __forceinline__ void sg_epilogue(const GemmArgs& g, const f32x16 (&ac
                 for (int v = 0; v < 8; ++v) g8[v] = acc[ti][tj][8 * b + v];
                 p[b] = sg_part8<KIND>(w8, g8, s, qmin, qmax);
             }
-            const float b0 = p[0] + __shfl_xor(p[0], 32);
-            const float b1 = p[1] + __shfl_xor(p[1], 32);
+            const float b0 = p[0] + xor32(p[0]);
+            const float b1 = p[1] + xor32(p[1]);
             if (lane < 32) {
                 if (!sg.part32) {
                     float* o = sg.out + wrow * (K >> 4) + (jt >> 4);   // 4-byte aligned only
@@ -487,8 +495,8 @@ struct SgEpiLds {
                     for (int v = 0; v < 8; ++v) g8[v] = acc[ti][tj][8 * b + v];
                     p[b] = sg_part8<KIND>(w8, g8, sc, qmin, qmax);
                 }
-                const float b0 = p[0] + __shfl_xor(p[0], 32);
-                const float b1 = p[1] + __shfl_xor(p[1], 32);
+                const float b0 = p[0] + xor32(p[0]);
+                const float b1 = p[1] + xor32(p[1]);
                 if (lane < 32) {
                     if (!sg.part32) {
                         float* o = sg.out + wrow * (K >> 4) + (jt >> 4);
