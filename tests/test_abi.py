@@ -61,7 +61,7 @@ def test_binding_enums_match_the_header():
         assert h["FQ_BUF_" + n.upper()] == v
     for n, v in F.DISTILL_TYPES.items():
         assert h["FQ_DISTILL_" + n.upper()] == v
-    # the values the design notes record where the ABI departs from the survey's sketch
+    # the published values of the kind and source enums (callers may store them)
     assert (h["FQ_NONE"], h["FQ_NVFP4"], h["FQ_INT"], h["FQ_FP8E4M3"]) == (0, 1, 2, 3)
     assert (h["FQ_LEARNABLE"], h["FQ_STATIC"], h["FQ_DYNAMIC"]) == (0, 1, 2)
 
