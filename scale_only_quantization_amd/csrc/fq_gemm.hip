@@ -83,6 +83,43 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// The same resource as four wave-uniform dwords, for stage_load below.
+__device__ __forceinline__ u32x4 make_rsrc_words(const void* base, int64_t bytes) {
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0xFFFFFFF0ll) bytes = 0xFFFFFFF0ll;
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);     // stride 0
+    r.z = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    r.w = 0x00020000u;
+    return r;
+}
+
+// A vector-memory instruction may read an SGPR that a vector instruction
+// wrote (v_readfirstlane) only five wait states later; the compiler inserts
+// those for its own instructions, not for assembly.  Called once a resource
+// is formed (it takes the resource as an operand, so it follows the writes),
+// before any stage_load reads it.
+__device__ __forceinline__ void rsrc_settle(const u32x4& rs) { asm volatile("s_nop 4" ::"s"(rs)); }
+
+// One wave's direct global->LDS load of a stage: 16 B per lane from
+// resource offset voff + soff into 1 KB of LDS at `dst` (wave-uniform; lane l
+// writes dst + 16 l).  Written as assembly so that the compiler does not see
+// an LDS write in flight: it would otherwise wait for every such load
+// (vmcnt(0)) before the next transposing LDS read, i.e. put the latency of
+// the step's loads just issued in front of the current step's fragment
+// reads.  Callers order these loads against the LDS reads themselves, with
+// their own vmcnt waits and barriers.  M0 carries the LDS address (one wait
+// state between its write and the load).
+__device__ __forceinline__ void stage_load(const u32x4& rs, lds_t* dst, uint32_t voff, uint32_t soff) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m), "v"(voff), "s"(rs), "s"(soff)
+                 : "memory", "m0");
+}
+
 // x of lane l ^ 32: one cross-half swap (v_permlane32_swap) and a select, no
 // LDS round trip.  The swap returns (lanes 0-31 of x in both halves, lanes
 // 32-63 of x in both halves).
@@ -91,15 +128,26 @@ __device__ __forceinline__ float xor32(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// s_waitcnt vmcnt(N) through the builtin, so that the compiler's own wait
+// bookkeeping sees it (the loads it tracks that are older than the N most
+// recent count as complete, as they are), then a compiler barrier, so that
+// no memory access moves across the wait.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);   // expcnt, lgkmcnt: no wait
+    asm volatile("" ::: "memory");
+}
+
 // Wait until at most n (clamped to 0..3) steps of L load instructions each
 // are outstanding: vector-memory loads complete in issue order.
 template <int L>
 __device__ __forceinline__ void wait_steps(int n) {
     static_assert(3 * L <= 63, "vmcnt range");
-    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
-    else if (n == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
-    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L) : "memory");
+    if (n <= 0) vm_wait<0>();
+    else if (n == 1) vm_wait<L>();
+    else if (n == 2) vm_wait<2 * L>();
+    else vm_wait<3 * L>();
 }
 
 // K-contiguous operand tile [ROWS][BK]: element (row, k) at byte row*ld2 + 2k
@@ -121,9 +169,9 @@ struct KTile {
     __device__ static __forceinline__ int off(int row, int ch) {   // byte offset of 16-B chunk
         return row * RB + ((ch ^ swz(row)) << 4);
     }
-    __amdgpu_buffer_rsrc_t rs;
+    u32x4 rs;
     uint32_t voff[PER_WAVE];
-    __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t r, int64_t ld) {
+    __device__ __forceinline__ void init(const u32x4& r, int64_t ld) {
         rs = r;
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -133,12 +181,12 @@ struct KTile {
             const int lc = (lane % CPR) ^ swz(row);       // logical chunk stored at this position
             voff[i] = (uint32_t)(row * ld * 2 + lc * 16);
         }
+        rsrc_settle(rs);
     }
     __device__ __forceinline__ void issue(lds_t* tile, int k0) {
         const int w = wave_id();
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + w) * 1024, 16, voff[i], k0 * 2, 0, 0);
+        for (int i = 0; i < PER_WAVE; ++i) stage_load(rs, tile + (NW * i + w) * 1024, voff[i], (uint32_t)k0 * 2);
     }
     // fragment of the 32x32x16 MFMA: row `row0 + lane%32`, k = 16 kk + 8 (lane/32) .. +7
     __device__ static __forceinline__ bf16x8 frag(const lds_t* tile, int row0, int kk) {
@@ -176,10 +224,10 @@ struct MNTile {
     __device__ static __forceinline__ int off(int k, int byte) {   // swizzled byte offset
         return k * RB + (phys(k, byte >> 4) << 4) + (byte & 15);
     }
-    __amdgpu_buffer_rsrc_t rs;
+    u32x4 rs;
     uint32_t voff[PER_WAVE];
     uint32_t ld2;
-    __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t r, int64_t ld) {
+    __device__ __forceinline__ void init(const u32x4& r, int64_t ld) {
         rs = r;
         ld2 = (uint32_t)(ld * 2);
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -191,13 +239,13 @@ struct MNTile {
             const int lc = pc ^ ((k & 3) << 1) ^ ((((pc >> 1) ^ k) & 1) << 3);   // phys(k, lc) == pc
             voff[i] = (uint32_t)(k * ld * 2 + lc * 16);
         }
+        rsrc_settle(rs);
     }
     __device__ __forceinline__ void issue(lds_t* tile, int k0) {
         const int w = wave_id();
         const uint32_t so = (uint32_t)k0 * ld2;          // wave-uniform: the scalar offset
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, tile + (NW * i + w) * 1024, 16, voff[i], so, 0, 0);
+        for (int i = 0; i < PER_WAVE; ++i) stage_load(rs, tile + (NW * i + w) * 1024, voff[i], so);
     }
     __device__ static __forceinline__ bf16x8 frag(const lds_t* tile, int row0, int kk) {
         const int lane = threadIdx.x & 63;
@@ -466,7 +514,7 @@ struct SgEpiLds {
 #pragma unroll
         for (int ti = 0; ti < WTM; ++ti) {
             lds_t* slot = slots + (ti & 1) * 4096;
-            if (ti == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // slices 2 and 3 have landed
+            if (ti == 2) vm_wait<0>();                  // slices 2 and 3 have landed
             const int64_t wrow = (int64_t)e * N + i_w + ti * 32 + (lane & 31);
             uint2 wv[WTN][4];
 #pragma unroll
@@ -713,12 +761,12 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         const int n0 = nt * BN;
         const int nk = g.K / BK;
         // rows past the routed rows read as zero (their outputs are not stored)
-        la.init(make_rsrc(g.A + m0 * g.lda, (g.R - m0) * g.lda * 2), g.lda);
+        la.init(make_rsrc_words(g.A + m0 * g.lda, (g.R - m0) * g.lda * 2), g.lda);
         const uint16_t* Be = g.B + (int64_t)e * g.strideB;
         if constexpr (MODE == FWD)
-            lb.init(make_rsrc(Be + (int64_t)n0 * g.ldb, (int64_t)BN * g.ldb * 2), g.ldb);
+            lb.init(make_rsrc_words(Be + (int64_t)n0 * g.ldb, (int64_t)BN * g.ldb * 2), g.ldb);
         else
-            lb.init(make_rsrc(Be + n0, ((int64_t)g.K - 1) * g.ldb * 2 + (int64_t)BN * 2), g.ldb);
+            lb.init(make_rsrc_words(Be + n0, ((int64_t)g.K - 1) * g.ldb * 2 + (int64_t)BN * 2), g.ldb);
         zero_acc();
         if constexpr (PP) mainloop_pp(nk, 0, no_hook);
         else mainloop(nk, 0, no_hook);
@@ -793,8 +841,8 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             const int me = (int)(min((int64_t)g.offsets[e + 1], g.R) - rb);
             nk = (me + BK - 1) / BK;
             // bounded to the expert's rows: the last reduction step's tail reads zeros
-            la.init(make_rsrc(g.A + rb * g.lda + i0, (int64_t)me * g.lda * 2 - i0 * 2), g.lda);
-            lb.init(make_rsrc(g.B + rb * g.ldb + n0, (int64_t)me * g.ldb * 2 - n0 * 2), g.ldb);
+            la.init(make_rsrc_words(g.A + rb * g.lda + i0, (int64_t)me * g.lda * 2 - i0 * 2), g.lda);
+            lb.init(make_rsrc_words(g.B + rb * g.ldb + n0, (int64_t)me * g.ldb * 2 - n0 * 2), g.ldb);
         };
         if (threadIdx.x == 0) {
             s_slot = atomicAdd(g.wg_ctr + x, 1);
@@ -826,12 +874,6 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             const bool more = next >= 0 && next < tiles_x;
             int after = 0;
             if (threadIdx.x == 0 && more) after = atomicAdd(g.wg_ctr + x, 1);
-            if (LDS_EPI && g.sg.out) {
-                ws.init(g.sg.W + ((int64_t)e * g.N + i0 + (wu / WVN) * 32 * WTM) * g.K + n0 + (wu % WVN) * 32 * WTN,
-                        g.K, 32 * WTM);
-                ws.issue(wslots, 0);
-                ws.issue(wslots + 4096, 1);
-            }
             const int ce = e, ci0 = i0, cn0 = n0;
             if (more) {
                 setup(next);
@@ -841,6 +883,13 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
                 const int iw = ci0 + wm * 32 * WTM, jw = cn0 + wn * 32 * WTN;
                 auto lds_epi = [&](auto kind_c) {
                     constexpr int KIND = decltype(kind_c)::value;
+                    // the wave's first two weight slices (its other two are
+                    // loaded as the first two are reduced)
+                    ws.init(g.sg.W + ((int64_t)ce * g.N + ci0 + (wu / WVN) * 32 * WTM) * g.K + cn0 +
+                                (wu % WVN) * 32 * WTN,
+                            g.K, 32 * WTM);
+                    ws.issue(wslots, 0);
+                    ws.issue(wslots + 4096, 1);
                     SgEpiLds<KIND, WTM, WTN> ep;
                     ep.begin(g, ce, iw, jw, lane);
                     ep.template run<LOADS>(g, acc, ce, iw, jw, lane, ws, wslots, 0);
