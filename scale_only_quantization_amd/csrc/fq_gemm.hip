@@ -96,28 +96,47 @@ __device__ __forceinline__ u32x4 make_rsrc_words(const void* base, int64_t bytes
     return r;
 }
 
-// A vector-memory instruction may read an SGPR that a vector instruction
-// wrote (v_readfirstlane) only five wait states later; the compiler inserts
-// those for its own instructions, not for assembly.  Called once a resource
-// is formed (it takes the resource as an operand, so it follows the writes),
-// before any stage_load reads it.
-__device__ __forceinline__ void rsrc_settle(const u32x4& rs) { asm volatile("s_nop 4" ::"s"(rs)); }
-
-// One wave's direct global->LDS load of a stage: 16 B per lane from
-// resource offset voff + soff into 1 KB of LDS at `dst` (wave-uniform; lane l
-// writes dst + 16 l).  Written as assembly so that the compiler does not see
-// an LDS write in flight: it would otherwise wait for every such load
-// (vmcnt(0)) before the next transposing LDS read, i.e. put the latency of
-// the step's loads just issued in front of the current step's fragment
-// reads.  Callers order these loads against the LDS reads themselves, with
-// their own vmcnt waits and barriers.  M0 carries the LDS address (one wait
-// state between its write and the load).
-__device__ __forceinline__ void stage_load(const u32x4& rs, lds_t* dst, uint32_t voff, uint32_t soff) {
+// One wave's direct global->LDS loads of a stage: N loads of 16 B per lane,
+// load i from resource offset voff[i] + soff into the 1 KB of LDS at
+// dst + i * STEP (dst wave-uniform; lane l writes 16 B at + 16 l).  Written as
+// assembly so that the compiler does not see LDS writes in flight: it would
+// otherwise wait for every such load (vmcnt(0)) before the next transposing
+// LDS read, i.e. put the latency of the step's loads just issued in front of
+// the current step's fragment reads.  Callers order these loads against the
+// LDS reads themselves, with their own vmcnt waits and barriers.  M0 carries
+// each load's LDS address (one wait state between its write and the load);
+// the leading s_nop 4 gives the five wait states a vector-memory read of an
+// SGPR needs after a vector instruction wrote it (v_readfirstlane, or
+// v_readlane restoring a spilled SGPR), which the compiler supplies for its
+// own instructions but not for assembly.
+template <int N, int STEP>
+__device__ __forceinline__ void stage_loads(const u32x4& rs, lds_t* dst, const uint32_t (&voff)[N], uint32_t soff) {
+    static_assert(N == 1 || N == 2 || N == 4, "loads per wave and stage");
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(m), "v"(voff), "s"(rs), "s"(soff)
-                 : "memory", "m0");
+#define FQ_LDS_LOAD(V) "s_nop 0\n\tbuffer_load_dwordx4 " V ", %[r], %[so] offen lds\n\t"
+    if constexpr (N == 1) {
+        asm volatile("s_nop 4\n\ts_mov_b32 m0, %[m]\n\t" FQ_LDS_LOAD("%[v0]")
+                     :
+                     : [m] "s"(m), [v0] "v"(voff[0]), [r] "s"(rs), [so] "s"(soff)
+                     : "memory", "m0");
+    } else if constexpr (N == 2) {
+        asm volatile("s_nop 4\n\ts_mov_b32 m0, %[m]\n\t" FQ_LDS_LOAD("%[v0]")
+                     "s_add_i32 m0, %[m], %[d1]\n\t" FQ_LDS_LOAD("%[v1]")
+                     :
+                     : [m] "s"(m), [v0] "v"(voff[0]), [v1] "v"(voff[1]), [r] "s"(rs), [so] "s"(soff),
+                       [d1] "n"(STEP)
+                     : "memory", "m0");
+    } else {
+        asm volatile("s_nop 4\n\ts_mov_b32 m0, %[m]\n\t" FQ_LDS_LOAD("%[v0]")
+                     "s_add_i32 m0, %[m], %[d1]\n\t" FQ_LDS_LOAD("%[v1]")
+                     "s_add_i32 m0, %[m], %[d2]\n\t" FQ_LDS_LOAD("%[v2]")
+                     "s_add_i32 m0, %[m], %[d3]\n\t" FQ_LDS_LOAD("%[v3]")
+                     :
+                     : [m] "s"(m), [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]),
+                       [r] "s"(rs), [so] "s"(soff), [d1] "n"(STEP), [d2] "n"(2 * STEP), [d3] "n"(3 * STEP)
+                     : "memory", "m0");
+    }
+#undef FQ_LDS_LOAD
 }
 
 // x of lane l ^ 32: one cross-half swap (v_permlane32_swap) and a select, no
@@ -181,12 +200,9 @@ struct KTile {
             const int lc = (lane % CPR) ^ swz(row);       // logical chunk stored at this position
             voff[i] = (uint32_t)(row * ld * 2 + lc * 16);
         }
-        rsrc_settle(rs);
     }
     __device__ __forceinline__ void issue(lds_t* tile, int k0) {
-        const int w = wave_id();
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) stage_load(rs, tile + (NW * i + w) * 1024, voff[i], (uint32_t)k0 * 2);
+        stage_loads<PER_WAVE, NW * 1024>(rs, tile + wave_id() * 1024, voff, (uint32_t)k0 * 2);
     }
     // fragment of the 32x32x16 MFMA: row `row0 + lane%32`, k = 16 kk + 8 (lane/32) .. +7
     __device__ static __forceinline__ bf16x8 frag(const lds_t* tile, int row0, int kk) {
@@ -239,13 +255,9 @@ struct MNTile {
             const int lc = pc ^ ((k & 3) << 1) ^ ((((pc >> 1) ^ k) & 1) << 3);   // phys(k, lc) == pc
             voff[i] = (uint32_t)(k * ld * 2 + lc * 16);
         }
-        rsrc_settle(rs);
     }
     __device__ __forceinline__ void issue(lds_t* tile, int k0) {
-        const int w = wave_id();
-        const uint32_t so = (uint32_t)k0 * ld2;          // wave-uniform: the scalar offset
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) stage_load(rs, tile + (NW * i + w) * 1024, voff[i], so);
+        stage_loads<PER_WAVE, NW * 1024>(rs, tile + wave_id() * 1024, voff, (uint32_t)k0 * ld2);
     }
     __device__ static __forceinline__ bf16x8 frag(const lds_t* tile, int row0, int kk) {
         const int lane = threadIdx.x & 63;
