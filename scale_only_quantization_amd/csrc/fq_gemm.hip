@@ -16,8 +16,9 @@
 // rows (the WGRAD reduction tail) read as zero.  A reduction step is BK deep;
 // S LDS stages are in flight, so a tile's loads are issued S-1 steps before
 // its MFMAs.  The stages of A come first in LDS, then those of B.  The large
-// FWD and DGRAD tiles run a ping-pong schedule (two groups of four waves, one
-// phase apart; see mainloop_pp).
+// tiles run a ping-pong schedule (two groups of four waves, one phase apart;
+// see mainloop_pp): FWD and DGRAD with BK = 64 and two stages, WGRAD with
+// BK = 32 and three.
 //   K-contiguous operand: LDS [rows][BK], the 16-B chunk index XORed with a
 //     row swizzle; a fragment (8 consecutive k of one row) is one
 //     ds_read_b128, and the 16 rows of one read pass fall on distinct banks.
@@ -43,8 +44,8 @@
 #define GEMM_S_BIG 2
 #endif
 #ifndef GEMM_BK_WG
-#define GEMM_BK_WG 64       // the same for the large WGRAD tile
-#define GEMM_S_WG 2
+#define GEMM_BK_WG 32       // the same for the large WGRAD tile
+#define GEMM_S_WG 3
 #endif
 #ifndef GEMM_XCD
 #define GEMM_XCD 1          // contiguous tile runs per XCD for FWD/DGRAD
@@ -57,7 +58,7 @@
 #define GEMM_PP 1           // ping-pong schedule of the 8-wave tile (FWD, DGRAD)
 #endif
 #ifndef GEMM_PP_WG
-#define GEMM_PP_WG 0        // the same for WGRAD
+#define GEMM_PP_WG 1        // the same for WGRAD
 #endif
 
 namespace fq {
@@ -718,10 +719,10 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
     // 0's memory phase of step kt+1.  Prologue: group 0 has steps [0, S-2] in
     // flight, group 1 steps [0, S-1]; pre: steps [0, pre) were issued by every
     // wave before the call.
-    // (with 64-deep steps and two stages the weight gradient keeps the
-    // single-phase loop: with both operands read transposed its memory phase
-    // outlasts a compute phase and the step's fragments spill; measured 7-12%
-    // slower)
+    // The weight gradient runs it with 32-deep steps and three stages: with
+    // 64-deep steps a step's fragments (both operands read transposed) do not
+    // fit the registers beside the accumulators, and with three 32-deep
+    // stages its loads have the same lead in time as two 64-deep ones.
     constexpr bool PP = GEMM_PP && NW == 8 && WVM == 2 && (MODE != WGRAD || GEMM_PP_WG);
     auto mainloop_pp = [&](int nk, int pre, auto&& first) {
         const int grp = wave_id() >> 2;
