@@ -102,6 +102,23 @@ __device__ __forceinline__ void e2m1_round2(float a0, float a1, float* q0, float
     *q0 = b.x;
     *q1 = b.y;
 }
+// E2M1 grid values (RNE) of eight quotients: the four pairs go into the four
+// bytes of one packed word and back.  The conversion saturates: beyond +-6,
+// infinities and NaN give +-6 with the operand's sign bit (measured on
+// gfx950), so it needs no clamp; a caller that must take the sign from
+// elsewhere (a NaN's sign after arithmetic is not defined) copies it after.
+__device__ __forceinline__ void e2m1_round8(const float* r, float* q) {
+    unsigned p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, r[2], r[3], 1.0f, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, r[4], r[5], 1.0f, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, r[6], r[7], 1.0f, 3);
+    const f32x2_cvt b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
+    const f32x2_cvt b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 1);
+    const f32x2_cvt b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 2);
+    const f32x2_cvt b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 3);
+    q[0] = b0.x; q[1] = b0.y; q[2] = b1.x; q[3] = b1.y;
+    q[4] = b2.x; q[5] = b2.y; q[6] = b3.x; q[7] = b3.y;
+}
 // 3-bit magnitude code of an E2M1 grid value: from 1 up, exponent and top
 // mantissa bit of the fp32 pattern; below 1 (0 or 0.5), 2 qm read off the low
 // bits of 2 qm + 2^23.  Both formed, one selected: no divergent branch.
@@ -219,8 +236,22 @@ __device__ __forceinline__ void quant_group(const float* x, float s, float qmin,
         Elem e[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) e[i] = quant_fast_r<KIND>(x[i], dv, qmin, qmax);
+        if constexpr (KIND == K_NVFP4 && N % 8 == 0) {
+            // saturating conversion of the signed quotients, sign from x: the
+            // same values as copysign(e2m1(min(|r|, 6)), x) for every r
 #pragma unroll
-        for (int i = 0; i < N; i += 2) grid_q2<KIND>(e[i], e[i + 1], x[i], x[i + 1], qmin, qmax);
+            for (int i = 0; i < N; i += 8) {
+                float rr[8], qq[8];
+#pragma unroll
+                for (int v = 0; v < 8; ++v) rr[v] = e[i + v].r;
+                e2m1_round8(rr, qq);
+#pragma unroll
+                for (int v = 0; v < 8; ++v) e[i + v].q = copysignf(qq[v], x[i + v]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; i += 2) grid_q2<KIND>(e[i], e[i + 1], x[i], x[i + 1], qmin, qmax);
+        }
 #pragma unroll
         for (int i = 0; i < N; ++i) f(i, e[i]);
     } else {

@@ -310,27 +310,10 @@ __device__ __forceinline__ int xcd_tile(int id, int grid, int tiles) {
     return (id / 8 < chunk && t < tiles) ? t : -1;
 }
 
-// E2M1 grid values (RNE) of eight signed quotients: the four pairs go into
-// the four bytes of one packed word and back.  The conversion saturates,
-// so quotients beyond +-6 give +-6 with no clamp (checked on gfx950 for
-// inputs up to 1e30, ties to even at 0.25, 0.75, 2.5, 3.5 and 5).
-__device__ __forceinline__ void e2m1_round8(const float* r, float* q) {
-    uint32_t p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], 1.0f, 0);
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, r[2], r[3], 1.0f, 1);
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, r[4], r[5], 1.0f, 2);
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, r[6], r[7], 1.0f, 3);
-    const f32x2_cvt b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
-    const f32x2_cvt b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 1);
-    const f32x2_cvt b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 2);
-    const f32x2_cvt b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 3);
-    q[0] = b0.x; q[1] = b0.y; q[2] = b1.x; q[3] = b1.y;
-    q[4] = b2.x; q[5] = b2.y; q[6] = b3.x; q[7] = b3.y;
-}
-
 // sum of g c over 8 elements sharing the effective scale s.  On the fast
 // path (every lane's scale normal) the NVFP4 grid value is converted from the
-// signed quotient directly: c = q - r only needs q's value, and a zero
-// element has c = 0 whatever the sign of its q.
+// signed quotient directly (the conversion saturates): c = q - r only needs
+// q's value, and a zero element has c = 0 whatever the sign of its q.
 template <int KIND>
 __device__ __forceinline__ float sg_part8(const float* w8, const float* g8, float s, float qmin, float qmax) {
     float part = 0.0f;
