@@ -141,13 +141,12 @@ __device__ __forceinline__ float rcp_rn(float d) {
 }
 
 struct Div {
-    float s, inv;
+    float s, inv;      // inv: RN(1/s), meaningful (and used) only when fast
     bool fast;
     __device__ __forceinline__ void set(float s_) {
         s = s_;
         fast = (s_ >= 0x1p-120f) && (s_ <= 0x1p120f);
         inv = rcp_rn(s_);
-        if (!fast) inv = 1.0f / s_;
     }
     __device__ __forceinline__ float operator()(float x) const {
         if (fast) {
