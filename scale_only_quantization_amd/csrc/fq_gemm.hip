@@ -707,7 +707,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
     // fit the registers beside the accumulators, and with three 32-deep
     // stages its loads have the same lead in time as two 64-deep ones.
     constexpr bool PP = GEMM_PP && NW == 8 && WVM == 2 && (MODE != WGRAD || GEMM_PP_WG);
-    auto mainloop_pp = [&](int nk, int pre, auto&& first) {
+    auto mainloop_pp = [&](int nk, int pre, auto&& first, auto&& tail0) {
         const int grp = wave_id() >> 2;
         bf16x8 af[KS][WTM], bfr[KS][WTN];
         fa.prep(wm * 32 * WTM);
@@ -759,7 +759,12 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             for (int u = 0; u < S; ++u)
                 if (kt + u < nk) phases(kt + u, u);
         }
-        if (grp == 0) bar();
+        // group 0 is done; while group 1 runs its last compute phase (no LDS
+        // reads, no loads in flight) group 0 may use LDS
+        if (grp == 0) {
+            tail0();
+            bar();
+        }
     };
     auto no_hook = []() {};
 
@@ -782,8 +787,6 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         else
             lb.init(make_rsrc_words(Be + n0, ((int64_t)g.K - 1) * g.ldb * 2 + (int64_t)BN * 2), g.ldb);
         zero_acc();
-        if constexpr (PP) mainloop_pp(nk, 0, no_hook);
-        else mainloop(nk, 0, no_hook);
         // Epilogue through LDS, so that global stores are whole row segments:
         // lane holds C[m = lane%32][n = 8*(v/4) + 4*(lane/32) + v%4] of each
         // 32x32 tile; it is written as bf16 into an LDS tile [BM][BN] whose
@@ -791,21 +794,32 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         // two rows per instruction (16 B per lane) to C.
         constexpr int RB = BN * 2, CH = BN / 8;                 // row bytes, 16-B chunks per row
         static_assert(BM * RB <= SMEM, "C tile fits the LDS");
-        __syncthreads();                                         // every wave is done with the stages
+        auto write_c = [&]() {
 #pragma unroll
-        for (int ti = 0; ti < WTM; ++ti) {
-            const int row = wm * 32 * WTM + ti * 32 + (lane & 31);
+            for (int ti = 0; ti < WTM; ++ti) {
+                const int row = wm * 32 * WTM + ti * 32 + (lane & 31);
 #pragma unroll
-            for (int tj = 0; tj < WTN; ++tj) {
+                for (int tj = 0; tj < WTN; ++tj) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = wn * 32 * WTN + tj * 32 + 8 * q + 4 * (lane >> 5);
-                    const int off = row * RB + (((col >> 3) ^ (row & 15)) << 4) + (col & 7) * 2;
-                    *reinterpret_cast<__attribute__((address_space(3))) uint64_t*>(smem + off) =
-                        (uint64_t)pack_bf16(acc[ti][tj][4 * q], acc[ti][tj][4 * q + 1]) |
-                        ((uint64_t)pack_bf16(acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]) << 32);
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = wn * 32 * WTN + tj * 32 + 8 * q + 4 * (lane >> 5);
+                        const int off = row * RB + (((col >> 3) ^ (row & 15)) << 4) + (col & 7) * 2;
+                        *reinterpret_cast<__attribute__((address_space(3))) uint64_t*>(smem + off) =
+                            (uint64_t)pack_bf16(acc[ti][tj][4 * q], acc[ti][tj][4 * q + 1]) |
+                            ((uint64_t)pack_bf16(acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]) << 32);
+                    }
                 }
             }
+        };
+        if constexpr (PP) {
+            // group 0 (rows 0..BM/2) writes its rows during group 1's last
+            // compute phase, group 1 after it
+            mainloop_pp(nk, 0, no_hook, write_c);
+            if (wave_id() >= 4) write_c();
+        } else {
+            mainloop(nk, 0, no_hook);
+            __syncthreads();                                     // every wave is done with the stages
+            write_c();
         }
         __syncthreads();
         constexpr int RPI = 64 / CH;                             // rows per wave instruction
@@ -881,7 +895,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         WStage ws;
         for (int tcount = 0;; ++tcount) {
             zero_acc();
-            if constexpr (PP) mainloop_pp(nk, PRE, no_hook);
+            if constexpr (PP) mainloop_pp(nk, PRE, no_hook, no_hook);
             else mainloop(nk, PRE, no_hook);
             __syncthreads();          // LDS stages free; s_q[(tcount - 1) & 1] written before the main loop
             const int next = s_q[(tcount - 1) & 1];
