@@ -495,9 +495,9 @@ struct SgEpiLds {
             return;
         }
         if (gran != G_GROUP) {
-            const float v = sg.scale[gran == G_ROW ? wrow : (int64_t)e];
-#pragma unroll
-            for (int tj = 0; tj < WTN; ++tj) sv[ti][tj][0] = sv[ti][tj][1] = v;
+            // one scale for the slice's row (or the matrix), read where used
+            // (copying it here would wait for the load at once)
+            sv[ti][0][0] = sg.scale[gran == G_ROW ? wrow : (int64_t)e];
             return;
         }
 #pragma unroll
@@ -547,7 +547,7 @@ struct SgEpiLds {
                 float p[2];
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    float sc = sv[ti][tj][b];
+                    float sc = sg.q.gran != G_GROUP ? sv[ti][0][0] : sv[ti][tj][b];
                     if (KIND == K_NVFP4) sc = t * e4m3_round(fminf(div_by_t(sc, t, inv_t, tfast), 448.0f));
                     const uint2 wa = wv[tj][2 * b], wb = wv[tj][2 * b + 1];
                     const float w8[8] = {bf_lo(wa.x), bf_hi(wa.x), bf_lo(wa.y), bf_hi(wa.y),
