@@ -112,7 +112,7 @@ __device__ __forceinline__ u32x4 make_rsrc_words(const void* base, int64_t bytes
 // own instructions but not for assembly.
 template <int N, int STEP>
 __device__ __forceinline__ void stage_loads(const u32x4& rs, lds_t* dst, const uint32_t (&voff)[N], uint32_t soff) {
-    static_assert(N == 1 || N == 2 || N == 4, "loads per wave and stage");
+    static_assert(N >= 1 && N <= 4, "loads per wave and stage");
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
 #define FQ_LDS_LOAD(V) "s_nop 0\n\tbuffer_load_dwordx4 " V ", %[r], %[so] offen lds\n\t"
     if constexpr (N == 1) {
@@ -126,6 +126,14 @@ __device__ __forceinline__ void stage_loads(const u32x4& rs, lds_t* dst, const u
                      :
                      : [m] "s"(m), [v0] "v"(voff[0]), [v1] "v"(voff[1]), [r] "s"(rs), [so] "s"(soff),
                        [d1] "n"(STEP)
+                     : "memory", "m0");
+    } else if constexpr (N == 3) {
+        asm volatile("s_nop 4\n\ts_mov_b32 m0, %[m]\n\t" FQ_LDS_LOAD("%[v0]")
+                     "s_add_i32 m0, %[m], %[d1]\n\t" FQ_LDS_LOAD("%[v1]")
+                     "s_add_i32 m0, %[m], %[d2]\n\t" FQ_LDS_LOAD("%[v2]")
+                     :
+                     : [m] "s"(m), [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [r] "s"(rs),
+                       [so] "s"(soff), [d1] "n"(STEP), [d2] "n"(2 * STEP)
                      : "memory", "m0");
     } else {
         asm volatile("s_nop 4\n\ts_mov_b32 m0, %[m]\n\t" FQ_LDS_LOAD("%[v0]")
