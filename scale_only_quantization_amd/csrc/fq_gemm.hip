@@ -715,7 +715,9 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
     // fit the registers beside the accumulators, and with three 32-deep
     // stages its loads have the same lead in time as two 64-deep ones.
     constexpr bool PP = GEMM_PP && NW == 8 && WVM == 2 && (MODE != WGRAD || GEMM_PP_WG);
-    auto mainloop_pp = [&](int nk, int pre, auto&& first, auto&& tail0) {
+    // nti: this wave's 32-row sub-tiles that hold valid rows (wave-uniform);
+    // below WTM the MFMAs and fragment reads of the others are skipped
+    auto mainloop_pp = [&](int nk, int pre, int nti, auto&& first, auto&& tail0) {
         const int grp = wave_id() >> 2;
         bf16x8 af[KS][WTM], bfr[KS][WTN];
         fa.prep(wm * 32 * WTM);
@@ -731,7 +733,8 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         wait_steps<LOADS>(min(last, nk - 1));
         bar();
         if (grp == 1) bar();
-        auto phases = [&](int kt, int st) {
+        auto phases = [&](int kt, int st, auto part_c) {
+            constexpr bool PART = decltype(part_c)::value;
             // memory phase
             if (grp == 0 && kt + S - 1 < nk) issue(kt + S - 1);
             const lds_t* sa = smem + st * A_BYTES;
@@ -739,9 +742,11 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-                for (int t = 0; t < WTM; ++t) af[kk][t] = fa.get(sa, t, kk);
+                for (int t = 0; t < WTM; ++t)
+                    if (!PART || t < nti) af[kk][t] = fa.get(sa, t, kk);
+                if (!PART || nti > 0)
 #pragma unroll
-                for (int t = 0; t < WTN; ++t) bfr[kk][t] = fb.get(sb, t, kk);
+                    for (int t = 0; t < WTN; ++t) bfr[kk][t] = fb.get(sb, t, kk);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (grp == 1) {
@@ -754,19 +759,25 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
                 for (int ti = 0; ti < WTM; ++ti)
+                    if (!PART || ti < nti)
 #pragma unroll
-                    for (int tj = 0; tj < WTN; ++tj)
-                        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][tj], af[kk][ti], acc[ti][tj],
-                                                                              0, 0, 0);
+                        for (int tj = 0; tj < WTN; ++tj)
+                            acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][tj], af[kk][ti],
+                                                                                  acc[ti][tj], 0, 0, 0);
             if (grp == 0) wait_steps<LOADS>(min(S - 2, nk - 2 - kt));
             bar();
         };
         first();
-        for (int kt = 0; kt < nk; kt += S) {
+        // full sub-tile sets keep the unpredicated loop
+        auto steps = [&](auto part_c) {
+            for (int kt = 0; kt < nk; kt += S) {
 #pragma unroll
-            for (int u = 0; u < S; ++u)
-                if (kt + u < nk) phases(kt + u, u);
-        }
+                for (int u = 0; u < S; ++u)
+                    if (kt + u < nk) phases(kt + u, u, part_c);
+            }
+        };
+        if (MODE == WGRAD || nti >= WTM) steps(std::false_type{});
+        else steps(std::true_type{});
         // group 0 is done; while group 1 runs its last compute phase (no LDS
         // reads, no loads in flight) group 0 may use LDS
         if (grp == 0) {
@@ -787,8 +798,9 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         const int64_t m_end = min((int64_t)g.offsets[e + 1], g.R);   // the tile's expert's rows
         const int n0 = nt * BN;
         const int nk = g.K / BK;
-        // rows past the routed rows read as zero (their outputs are not stored)
-        la.init(make_rsrc_words(g.A + m0 * g.lda, (g.R - m0) * g.lda * 2), g.lda);
+        // rows past the expert's rows read as zero, without memory traffic
+        // (their outputs are not stored)
+        la.init(make_rsrc_words(g.A + m0 * g.lda, max(m_end - m0, (int64_t)0) * g.lda * 2), g.lda);
         const uint16_t* Be = g.B + (int64_t)e * g.strideB;
         if constexpr (MODE == FWD)
             lb.init(make_rsrc_words(Be + (int64_t)n0 * g.ldb, (int64_t)BN * g.ldb * 2), g.ldb);
@@ -822,7 +834,9 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         if constexpr (PP) {
             // group 0 (rows 0..BM/2) writes its rows during group 1's last
             // compute phase, group 1 after it
-            mainloop_pp(nk, 0, no_hook, write_c);
+            // rows of this wave's sub-tiles that hold routed rows of the expert
+            const int wrows = (int)min((int64_t)BM, m_end - m0) - wm * 32 * WTM;
+            mainloop_pp(nk, 0, min(max((wrows + 31) / 32, 0), WTM), no_hook, write_c);
             if (wave_id() >= 4) write_c();
         } else {
             mainloop(nk, 0, no_hook);
@@ -903,7 +917,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         WStage ws;
         for (int tcount = 0;; ++tcount) {
             zero_acc();
-            if constexpr (PP) mainloop_pp(nk, PRE, no_hook, no_hook);
+            if constexpr (PP) mainloop_pp(nk, PRE, WTM, no_hook, no_hook);
             else mainloop(nk, PRE, no_hook);
             __syncthreads();          // LDS stages free; s_q[(tcount - 1) & 1] written before the main loop
             const int next = s_q[(tcount - 1) & 1];
