@@ -312,6 +312,13 @@ struct MNTile {
 // of tiles [x * chunk, (x + 1) * chunk), chunk = ceil(tiles / 8); tiles that
 // share operands (the N tiles of one row tile, the row tiles of one expert)
 // then meet in the same L2.  Returns -1 for ids past the tile count.
+// p[i] through the scalar cache, for an array the kernel does not write and a
+// wave-uniform i (a plain load after the kernel's own stores would be a
+// vector load, ordered behind every vector load in flight)
+__device__ __forceinline__ int32_t sload(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 __device__ __forceinline__ int xcd_tile(int id, int grid, int tiles) {
     const int chunk = (tiles + 7) / 8;
     const int t = (id % 8) * chunk + id / 8;
@@ -476,12 +483,13 @@ struct WStage {
 };
 
 // The epilogue above with the weights read from the wave's LDS slots, in two
-// parts.  begin(): the scales of slices 0 and 1 (issued, like slices 0 and 1
-// of the weights, before the next tile's first loads).  run(): waits until at
-// most `later` steps of L loads (the next tile's) are outstanding, then
-// reduces slice by slice; slice ti + 2 refills slice ti's slot as soon as
-// slice ti's weights are in registers.  A wait on the vector memory counter
-// also covers the direct-to-LDS loads; this wave alone reads its slots.
+// parts.  begin(): the scales of slices 0 and 1 (issued after slices 0 and 1
+// of the weights).  run(): waits until at most `later` steps of L loads are
+// outstanding, calls after_wait() (which issues the next tile's first loads),
+// then reduces slice by slice; slice ti + 2 refills slice ti's slot as soon
+// as slice ti's weights are in registers.  A wait on the vector memory
+// counter also covers the direct-to-LDS loads; this wave alone reads its
+// slots.
 template <int KIND, int WTM, int WTN>
 struct SgEpiLds {
     static_assert(WTN == 2 && WTM >= 2, "two 32-column tiles per wave, two slots");
@@ -520,9 +528,11 @@ struct SgEpiLds {
         load_sv(g, e, i_w, j_w, lane, 0);
         load_sv(g, e, i_w, j_w, lane, 1);
     }
-    template <int L>
+    // after_wait(): called once the first two slices and scales have landed
+    // (loads it issues overlap the reductions)
+    template <int L, typename F>
     __device__ __forceinline__ void run(const GemmArgs& g, const f32x16 (&acc)[WTM][WTN], int e, int i_w, int j_w,
-                                        int lane, const WStage& ws, lds_t* slots, int later) {
+                                        int lane, const WStage& ws, lds_t* slots, int later, F&& after_wait) {
         const SgArgs& sg = g.sg;
         const int64_t N = g.N, K = g.K;
         const float qmin = sg.q.qmin, qmax = sg.q.qmax;
@@ -533,6 +543,7 @@ struct SgEpiLds {
         const bool tfast = t >= 0x1p-120f && t <= 0x1p120f;
         const float inv_t = KIND == K_NVFP4 ? rcp_rn(t) : 0.0f;
         wait_steps<L>(later);
+        after_wait();
 #pragma unroll
         for (int ti = 0; ti < WTM; ++ti) {
             lds_t* slot = slots + (ti & 1) * 4096;
@@ -879,16 +890,17 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         const int x = blockIdx.x & 7;
         const int tj_n = g.K / BN;                     // output [N, K] per expert
         const int tpe = (g.N / BM) * tj_n;
-        const int tiles_x = min(max(g.wg_cnt[x], 0), g.E) * tpe;
+        const int tiles_x = min(max(sload(g.wg_cnt, x), 0), g.E) * tpe;
         int e = 0, i0 = 0, n0 = 0, nk = 0;
+        // slot: wave-uniform; the lists are read through the scalar cache
         auto setup = [&](int slot) {
             const int eo = slot / tpe;
             const int tt = slot - eo * tpe;
-            e = min(max(g.wg_list[x * g.E + eo], 0), g.E - 1);
+            e = min(max(sload(g.wg_list, x * g.E + eo), 0), g.E - 1);
             i0 = (tt / tj_n) * BM;
             n0 = (tt - (tt / tj_n) * tj_n) * BN;
-            const int64_t rb = g.offsets[e];
-            const int me = (int)(min((int64_t)g.offsets[e + 1], g.R) - rb);
+            const int64_t rb = sload(g.offsets, e);
+            const int me = (int)(min((int64_t)sload(g.offsets, e + 1), g.R) - rb);
             nk = (me + BK - 1) / BK;
             // bounded to the expert's rows: the last reduction step's tail reads zeros
             la.init(make_rsrc_words(g.A + rb * g.lda + i0, (int64_t)me * g.lda * 2 - i0 * 2), g.lda);
@@ -899,7 +911,7 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             s_q[1] = atomicAdd(g.wg_ctr + x, 1);       // tile 1's slot, read after tile 0's main loop
         }
         __syncthreads();
-        const int slot = s_slot;
+        const int slot = __builtin_amdgcn_readfirstlane(s_slot);
         if (slot < 0 || slot >= tiles_x) return;
         // The next tile's first PRE steps are issued before this tile's
         // epilogue, into stages [0, PRE); the fused epilogue's weights go
@@ -920,12 +932,16 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
             if constexpr (PP) mainloop_pp(nk, PRE, WTM, no_hook, no_hook);
             else mainloop(nk, PRE, no_hook);
             __syncthreads();          // LDS stages free; s_q[(tcount - 1) & 1] written before the main loop
-            const int next = s_q[(tcount - 1) & 1];
+            const int next = __builtin_amdgcn_readfirstlane(s_q[(tcount - 1) & 1]);
             const bool more = next >= 0 && next < tiles_x;
             int after = 0;
             if (threadIdx.x == 0 && more) after = atomicAdd(g.wg_ctr + x, 1);
             const int ce = e, ci0 = i0, cn0 = n0;
-            if (more) {
+            // With the weights staged through LDS the epilogue's own loads go
+            // first; the next tile's set-up loads overlap them, and its first
+            // steps are issued once they have landed.
+            const bool late = LDS_EPI && g.sg.out;
+            if (more && !late) {
                 setup(next);
                 issue_steps(nk, 0, PRE - 1);
             }
@@ -942,7 +958,10 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
                     ws.issue(wslots + 4096, 1);
                     SgEpiLds<KIND, WTM, WTN> ep;
                     ep.begin(g, ce, iw, jw, lane);
-                    ep.template run<LOADS>(g, acc, ce, iw, jw, lane, ws, wslots, 0);
+                    if (more) setup(next);
+                    ep.template run<LOADS>(g, acc, ce, iw, jw, lane, ws, wslots, 0, [&]() {
+                        if (more) issue_steps(nk, 0, PRE - 1);
+                    });
                 };
                 if constexpr (LDS_EPI) {
                     if (g.sg.q.kind == K_NVFP4) lds_epi(std::integral_constant<int, K_NVFP4>{});
