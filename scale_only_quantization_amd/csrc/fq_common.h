@@ -41,6 +41,18 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
                       pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
 }
 
+// ------------------------------------------------------------ scalar loads --
+// p[i] through the scalar cache when i is wave-uniform, for an array the
+// kernel does not write.  (A plain load in a kernel that also stores is a
+// vector load, and a wait for it waits for every vector memory operation
+// issued before it, stores included.)
+__device__ __forceinline__ int32_t sload(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+__device__ __forceinline__ float sload(const float* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) float*)p)[i];
+}
+
 // ------------------------------------------------------------- reductions ---
 // Fixed xor-butterfly trees: the same order on every call, so sums are
 // bitwise reproducible.

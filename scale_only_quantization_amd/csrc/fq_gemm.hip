@@ -312,13 +312,6 @@ struct MNTile {
 // of tiles [x * chunk, (x + 1) * chunk), chunk = ceil(tiles / 8); tiles that
 // share operands (the N tiles of one row tile, the row tiles of one expert)
 // then meet in the same L2.  Returns -1 for ids past the tile count.
-// p[i] through the scalar cache, for an array the kernel does not write and a
-// wave-uniform i (a plain load after the kernel's own stores would be a
-// vector load, ordered behind every vector load in flight)
-__device__ __forceinline__ int32_t sload(const int32_t* p, int64_t i) {
-    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
-}
-
 __device__ __forceinline__ int xcd_tile(int id, int grid, int tiles) {
     const int chunk = (tiles + 7) / 8;
     const int t = (id % 8) * chunk + id / 8;

@@ -262,12 +262,25 @@ __device__ __forceinline__ float act_scale(const ActQ& a, int e, float bm, float
                                            float* dfac) {
     *dfac = 1.0f;
     if (KIND == K_NVFP4) {
-        const float t = a.s[e];
-        const float d = e4m3_round(fminf(bm / (6.0f * t), 448.0f));
+        const float t = sload(a.s, e);
+        const float d6 = 6.0f * t;
+        // fl32(bm / d6): Markstein's corrected quotient when every lane's d6
+        // is normal, IEEE division otherwise.  Where the corrected form
+        // overflows (a NaN) the quotient is far above 448, and fminf takes
+        // 448 from both.
+        float qd;
+        if (__all(d6 >= 0x1p-120f && d6 <= 0x1p120f)) {
+            const float inv = rcp_rn(d6);
+            const float q0 = bm * inv;
+            qd = __builtin_fmaf(__builtin_fmaf(-q0, d6, bm), inv, q0);
+        } else {
+            qd = bm / d6;
+        }
+        const float d = e4m3_round(fminf(qd, 448.0f));
         *dfac = d;
         return t * d;
     }
-    if (a.q.source != S_DYNAMIC) return a.s[e];          // per-expert per-tensor scale
+    if (a.q.source != S_DYNAMIC) return sload(a.s, e);   // per-expert per-tensor scale
     if (a.q.gran == G_ROW) return row_s;
     return gm / a.q.qdiv;
 }
@@ -277,16 +290,22 @@ __device__ __forceinline__ void quant8(const float* f, float s, float qmin, floa
     quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& e) { y[i] = e.q * s; });
 }
 
-// straight-through terms of 8 elements: sum g*c, and the pass mask applied to g
-template <int KIND>
-__device__ __forceinline__ float ste8(const float* f, const float* g, float s, float qmin, float qmax,
-                                      bool dyn, float* gx) {
+// straight-through terms of 8 elements: sum g*c, and the pass mask applied to
+// g (a dynamic quantiser passes every element)
+template <int KIND, bool DYN>
+__device__ __forceinline__ float ste8_(const float* f, const float* g, float s, float qmin, float qmax, float* gx) {
     float part = 0.0f;
     quant_group<KIND, 8>(f, s, qmin, qmax, [&](int i, const Elem& el) {
         part = __builtin_fmaf(g[i], ste_c(el, qmin, qmax), part);
-        gx[i] = dyn ? g[i] : g[i] * (el.inside ? 1.0f : 0.0f);   // g * mask (signed zero)
+        gx[i] = DYN ? g[i] : g[i] * (el.inside ? 1.0f : 0.0f);   // g * mask (signed zero)
     });
     return part;
+}
+// dyn is uniform (the quantiser's source): one branch, not a select per element
+template <int KIND>
+__device__ __forceinline__ float ste8(const float* f, const float* g, float s, float qmin, float qmax,
+                                      bool dyn, float* gx) {
+    return dyn ? ste8_<KIND, true>(f, g, s, qmin, qmax, gx) : ste8_<KIND, false>(f, g, s, qmin, qmax, gx);
 }
 
 __device__ __forceinline__ float amax8(const float* f) {
