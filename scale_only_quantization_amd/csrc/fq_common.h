@@ -53,6 +53,17 @@ __device__ __forceinline__ float sload(const float* p, int64_t i) {
     return ((const __attribute__((address_space(4))) float*)p)[i];
 }
 
+// s_waitcnt vmcnt(N) through the builtin, so that the compiler's own wait
+// bookkeeping sees it (the loads it tracks that are older than the N most
+// recent count as complete, as they are), then a compiler barrier, so that
+// no memory access moves across the wait.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);   // expcnt, lgkmcnt: no wait
+    asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------- reductions ---
 // Fixed xor-butterfly trees: the same order on every call, so sums are
 // bitwise reproducible.

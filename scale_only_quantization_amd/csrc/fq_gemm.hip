@@ -156,17 +156,6 @@ __device__ __forceinline__ float xor32(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// s_waitcnt vmcnt(N) through the builtin, so that the compiler's own wait
-// bookkeeping sees it (the loads it tracks that are older than the N most
-// recent count as complete, as they are), then a compiler barrier, so that
-// no memory access moves across the wait.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);   // expcnt, lgkmcnt: no wait
-    asm volatile("" ::: "memory");
-}
-
 // Wait until at most n (clamped to 0..3) steps of L load instructions each
 // are outstanding: vector-memory loads complete in issue order.
 template <int L>

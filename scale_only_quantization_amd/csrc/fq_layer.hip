@@ -254,15 +254,21 @@ __global__ __launch_bounds__(TPB) void k_route_scatter(const int32_t* ids, int64
 }
 
 // --------------------------------------------------------------- activation --
-// Effective scale of an 8-element vector under the layer's activation
-// quantiser of expert e.  `bm` is the vector's 16-block amax (NVFP4), `gm`
-// its group amax (INT/FP8 per-group dynamic), `row_s` the dynamic per-row scale.
+// The per-expert tensor scale the quantiser reads (0 where it has none):
+// through the scalar cache when e is wave-uniform.
 template <int KIND>
-__device__ __forceinline__ float act_scale(const ActQ& a, int e, float bm, float gm, float row_s,
-                                           float* dfac) {
+__device__ __forceinline__ float act_t(const ActQ& a, int e) {
+    return (KIND == K_NVFP4 || (KIND != K_NONE && a.q.source != S_DYNAMIC)) ? sload(a.s, e) : 0.0f;
+}
+
+// Effective scale of an 8-element vector under the layer's activation
+// quantiser, given its expert's tensor scale t = act_t(a, e).  `bm` is the
+// vector's 16-block amax (NVFP4), `gm` its group amax (INT/FP8 per-group
+// dynamic), `row_s` the dynamic per-row scale.
+template <int KIND>
+__device__ __forceinline__ float act_scale_t(const ActQ& a, float t, float bm, float gm, float row_s, float* dfac) {
     *dfac = 1.0f;
     if (KIND == K_NVFP4) {
-        const float t = sload(a.s, e);
         const float d6 = 6.0f * t;
         // fl32(bm / d6): Markstein's corrected quotient when every lane's d6
         // is normal, IEEE division otherwise.  Where the corrected form
@@ -280,9 +286,15 @@ __device__ __forceinline__ float act_scale(const ActQ& a, int e, float bm, float
         *dfac = d;
         return t * d;
     }
-    if (a.q.source != S_DYNAMIC) return sload(a.s, e);   // per-expert per-tensor scale
+    if (a.q.source != S_DYNAMIC) return t;               // per-expert per-tensor scale
     if (a.q.gran == G_ROW) return row_s;
     return gm / a.q.qdiv;
+}
+
+// the same for expert e
+template <int KIND>
+__device__ __forceinline__ float act_scale(const ActQ& a, int e, float bm, float gm, float row_s, float* dfac) {
+    return act_scale_t<KIND>(a, act_t<KIND>(a, e), bm, gm, row_s, dfac);
 }
 
 template <int KIND>
@@ -440,24 +452,41 @@ __global__ __launch_bounds__(TPB) void k_swiglu_a2(SwigluArgs a) {
     for (int64_t r0 = ((int64_t)blockIdx.x * RPB + (threadIdx.x >> 6)) * RW; r0 < a.R;
          r0 += (int64_t)gridDim.x * RPB * RW) {
         int ex[RW];
+        float tx[RW];                                    // the rows' tensor scales, read before any store
 #pragma unroll
-        for (int i = 0; i < RW; ++i) ex[i] = r0 + i < a.R ? clamp_id(a.row_expert[r0 + i], a.E) : 0;
+        for (int i = 0; i < RW; ++i) {
+            ex[i] = r0 + i < a.R ? clamp_id(a.row_expert[r0 + i], a.E) : 0;
+            tx[i] = act_t<KIND>(a.a2, ex[i]);
+        }
         uint4 hv[NV];
         float bm[NV];
         float rm[RW];
 #pragma unroll
         for (int i = 0; i < RW; ++i) rm[i] = 0.0f;
+        // every vector's inputs first, then one wait
+        uint4 zg[NV], zu[NV];
 #pragma unroll
         for (int c = 0; c < NV; ++c) {
             const int u = lane + c * WAVE;
             const int ri = (RW == 2 && u >= nvec) ? 1 : 0;
             const int v = u - ri * nvec;
-            float h[8];
+            zg[c] = zu[c] = make_uint4(0, 0, 0, 0);
             if (u < RW * nvec && r0 + ri < a.R) {
                 const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + (r0 + ri) * 2 * (int64_t)a.I);
+                zg[c] = zr[v];
+                zu[c] = zr[v + nvec];
+            }
+        }
+        vm_wait<0>();
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            const int u = lane + c * WAVE;
+            const int ri = (RW == 2 && u >= nvec) ? 1 : 0;
+            float h[8];
+            if (u < RW * nvec && r0 + ri < a.R) {
                 float g[8], uu[8];
-                unpack8(zr[v], g);
-                unpack8(zr[v + nvec], uu);
+                unpack8(zg[c], g);
+                unpack8(zu[c], uu);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     float sig;
@@ -497,9 +526,9 @@ __global__ __launch_bounds__(TPB) void k_swiglu_a2(SwigluArgs a) {
             } else {
                 float h[8], y[8], dfac;
                 unpack8(hv[c], h);
-                const int e = RW == 2 && ri ? ex[RW - 1] : ex[0];
+                const float te = RW == 2 && ri ? tx[RW - 1] : tx[0];
                 const float rs = RW == 2 && ri ? row_s[RW - 1] : row_s[0];
-                quant8<KIND>(h, act_scale<KIND>(a.a2, e, bm[c], bm[c], rs, &dfac), qmin, qmax, y);
+                quant8<KIND>(h, act_scale_t<KIND>(a.a2, te, bm[c], bm[c], rs, &dfac), qmin, qmax, y);
                 dst[v] = pack8(y);
             }
         }
@@ -550,6 +579,7 @@ __global__ __launch_bounds__(TPB) void k_combine(CombineArgs a) {
 }
 
 // ------------------------------------------------------------- B1 permute dY --
+constexpr int KU = 8;                   // top-k of the unrolled path
 template <int NV>
 __global__ __launch_bounds__(TPB) void k_permute_dy(PermuteDyArgs a) {
     const int lane = threadIdx.x & (WAVE - 1);
@@ -557,6 +587,48 @@ __global__ __launch_bounds__(TPB) void k_permute_dy(PermuteDyArgs a) {
     for (int64_t t = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 6); t < a.T; t += (int64_t)gridDim.x * RPB) {
         const Slots sl = load_slots(nullptr, a.row_of, a.w, t, a.k, 1, a.T * a.k, lane);
         float d[NV][8];
+        if (nvec == NV * WAVE && a.dw && a.k == KU) {
+            // Every lane holds NV whole vectors and there are KU copies:
+            // straight-line code in which a wait names only the row it needs.
+            // Y_r row j+1 is loaded while row j is reduced, and it is issued
+            // before row j's stores, so no wait is for a store.
+            const uint4* dyt = reinterpret_cast<const uint4*>(a.dy + t * a.H);
+            uint4 dv[NV];
+#pragma unroll
+            for (int c = 0; c < NV; ++c) dv[c] = dyt[lane + c * WAVE];
+            uint4 yb[2][NV];
+            auto load_y = [&](int j, uint4* dst) {
+                const uint4* src = reinterpret_cast<const uint4*>(a.yr + (int64_t)slot_i(sl.row, j) * a.H);
+#pragma unroll
+                for (int c = 0; c < NV; ++c) dst[c] = src[lane + c * WAVE];
+            };
+            load_y(0, yb[0]);
+#pragma unroll
+            for (int c = 0; c < NV; ++c) unpack8(dv[c], d[c]);
+            float dwl = 0.0f;                            // lane j: copy j's d topk_w
+#pragma unroll
+            for (int j = 0; j < KU; ++j) {
+                if (j + 1 < KU) load_y(j + 1, yb[(j + 1) & 1]);
+                const float w = slot_f(sl.w, j);
+                const int64_t row = slot_i(sl.row, j);
+                uint4* dst = reinterpret_cast<uint4*>(a.dyr + row * a.H);
+                float part = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NV; ++c) {
+                    float o[8], yv[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) o[i] = w * d[c][i];
+                    dst[lane + c * WAVE] = pack8(o);
+                    unpack8(yb[j & 1][c], yv);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) part = __builtin_fmaf(d[c][i], yv[i], part);
+                }
+                part = wave_sum(part);
+                dwl = lane == j ? part : dwl;
+            }
+            if (lane < KU) a.dw[t * a.k + lane] = dwl;
+            continue;
+        }
 #pragma unroll
         for (int c = 0; c < NV; ++c) {
             const int v = lane + c * WAVE;
@@ -616,34 +688,44 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
     // need the forward's codec terms; per-row/group dynamic quantisers pass
     // the gradient straight and own no parameter.
     const bool recompute = KIND == K_NVFP4 || (KIND != K_NONE && !dyn);
+    // passes of the wave over its rows
+    const int npass = (RW * nvec + WAVE - 1) / WAVE;
     for (int64_t r0 = ((int64_t)blockIdx.x * RPB + (threadIdx.x >> 6)) * RW; r0 < a.R;
          r0 += (int64_t)gridDim.x * RPB * RW) {
         int ex[RW];
-        float part_row[RW];
+        float tx[RW], part_row[RW];
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
             ex[i] = r0 + i < a.R ? clamp_id(a.row_expert[r0 + i], a.E) : 0;
+            tx[i] = recompute ? act_t<KIND>(a.a2, ex[i]) : 0.0f;
             part_row[i] = 0.0f;
         }
-        for (int u0 = 0; u0 < RW * nvec; u0 += WAVE) {
-            const int uf = u0 + lane;
+        // pass p: this lane's vector (row r0 + ri, vector v) and its inputs
+        auto load_pass = [&](int p, uint4& zg, uint4& zu, uint4& zd) {
+            const int uf = p * WAVE + lane;
+            const int ri = (RW == 2 && uf >= nvec) ? 1 : 0;
+            const int v = uf - ri * nvec;
+            const int64_t r = r0 + ri;
+            if (uf < RW * nvec && r < a.R) {
+                const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + r * 2 * (int64_t)a.I);
+                zg = zr[v];
+                zu = zr[v + nvec];
+                zd = reinterpret_cast<const uint4*>(a.dhh + r * a.I)[v];
+            } else {
+                zg = zu = zd = make_uint4(0, 0, 0, 0);
+            }
+        };
+        auto run_pass = [&](int p, const uint4& zg, const uint4& zu, const uint4& zd) {
+            const int uf = p * WAVE + lane;
             const int ri = (RW == 2 && uf >= nvec) ? 1 : 0;
             const int v = uf - ri * nvec;
             const int64_t r = r0 + ri;
             const bool act = uf < RW * nvec && r < a.R;
-            const int e = RW == 2 && ri ? ex[RW - 1] : ex[0];
-            const uint4* zr = reinterpret_cast<const uint4*>(a.z1 + r * 2 * (int64_t)a.I);
-            const uint4* dr = reinterpret_cast<const uint4*>(a.dhh + r * a.I);
             uint4* out = reinterpret_cast<uint4*>(a.dz1 + r * 2 * (int64_t)a.I);
             float g[8], u[8], dh[8], sg[8], h[8];
-            if (act) {
-                unpack8(zr[v], g);
-                unpack8(zr[v + nvec], u);
-                unpack8(dr[v], dh);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) { g[i] = 0.0f; u[i] = 0.0f; dh[i] = 0.0f; }
-            }
+            unpack8(zg, g);
+            unpack8(zu, u);
+            unpack8(zd, dh);
             // silu and sigmoid as the forward forms them
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = silu_sig(g[i], &sg[i]) * u[i];
@@ -656,7 +738,8 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
                     bm = fmaxf(m, __shfl_xor(m, 1));
                 }
                 float dfac;
-                const float s = act_scale<KIND>(a.a2, e, bm, bm, 0.0f, &dfac);
+                const float te = RW == 2 && ri ? tx[RW - 1] : tx[0];
+                const float s = act_scale_t<KIND>(a.a2, te, bm, bm, 0.0f, &dfac);
                 float gx[8];
                 const float part = ste8<KIND>(hq, dh, s, qmin, qmax, dyn, gx);
                 if (act) {
@@ -679,6 +762,11 @@ __global__ __launch_bounds__(TPB) void k_swiglu_bwd(SwigluBwdArgs a) {
                 out[v] = pack8(dg);
                 out[v + nvec] = pack8(du);
             }
+        };
+        for (int p = 0; p < npass; ++p) {
+            uint4 zg, zu, zd;
+            load_pass(p, zg, zu, zd);
+            run_pass(p, zg, zu, zd);
         }
         if (a.rowpart) {
 #pragma unroll
@@ -729,6 +817,7 @@ __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
         const Slots sl = load_slots(a.ids, a.row_of, nullptr, t, a.k, a.E, a.T * a.k, lane);
+        float rp = 0.0f;
         for (int j = 0; j < a.k; ++j) {
             const int e = slot_i(sl.e, j);
             const int64_t row = slot_i(sl.row, j);
@@ -755,9 +844,12 @@ __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
             }
             if (a.rowpart) {
                 const float tot = wave_sum(part_row);
-                if (lane == 0) a.rowpart[row * SPLIT + hf] = tot;
+                rp = lane == j ? tot : rp;
             }
         }
+        // lane j holds copy j's row and partial: one store after the loop, so
+        // no load above waits behind a store
+        if (a.rowpart && lane < a.k) a.rowpart[(int64_t)sl.row * SPLIT + hf] = rp;
         if (a.dx) {
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
