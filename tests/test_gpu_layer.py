@@ -229,6 +229,15 @@ def test_layer_two_rows_per_wave(fmt, I):
     _full_parity(L, data, P, Po)
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "w8a8"])
+def test_layer_top8_whole_vector_rows(fmt):
+    # top-8 over rows of 2048 (four vectors of 8 per lane): the straight-line
+    # top-8 paths of the dY permute, and quarter rows in the A1 backward,
+    # checked element by element at a size the oracle finishes in seconds
+    L, data, P, Po = _case(fmt, 16, 2048, 768, 64, 8, routing_kind="zipf", seed=41)
+    _full_parity(L, data, P, Po)
+
+
 @pytest.mark.parametrize("H,I", [(8192, 256), (256, 8192)], ids=["hidden8192", "intermediate8192"])
 def test_layer_largest_hidden_and_intermediate(H, I):
     # the largest widths the library accepts (16 vectors of 8 per lane per row)
