@@ -211,6 +211,8 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
     // load = reduction steps of 64 rows + 2 for the epilogue.  One wave; lane
     // x < 8 keeps XCD x's load and list.  The experts come 64 at a time, one
     // per lane, and each step reads its expert and cost from a lane register.
+    // (A form with the eight loads in scalar registers measured slower: about
+    // 90 scalar instructions per step.)
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         int load = 0, n = 0;
@@ -221,10 +223,12 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* hist, int nblk, in
             for (int i = 0; i < nr; ++i) {
                 const int ex = __builtin_amdgcn_readlane(ex_l, i);
                 const int cost = __builtin_amdgcn_readlane(cost_l, i);
+                // minimum over lanes 0-7 by DPP moves (no LDS round trip):
+                // swap neighbours, swap pairs, then mirror the 8-lane half row
                 int key = lane < 8 ? load * 8 + lane : 0x7FFFFFFF;
-                key = min(key, __shfl_xor(key, 1));
-                key = min(key, __shfl_xor(key, 2));
-                key = min(key, __shfl_xor(key, 4));
+                key = min(key, __builtin_amdgcn_mov_dpp(key, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+                key = min(key, __builtin_amdgcn_mov_dpp(key, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+                key = min(key, __builtin_amdgcn_mov_dpp(key, 0x141, 0xF, 0xF, false));   // row_half_mirror
                 if (lane == (key & 7)) {
                     wg_list[lane * E + n] = ex;
                     ++n;

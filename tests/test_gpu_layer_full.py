@@ -150,6 +150,19 @@ def test_full_size_layer_sampled(case_name, fmt):
                              f"{n} expert {e}")
         print(f"[full] expert {e} ({hi - lo} rows) ok", flush=True)
 
+    # Every expert's weight-scale gradients, as a property: the weight-gradient
+    # kernel deals the experts' tiles out to the XCDs, so an expert it never
+    # reached would leave its gradients untouched.  Finite everywhere, and
+    # nonzero for each expert with routed rows (the gradient of a random
+    # layer vanishes nowhere in a whole expert's blocks).
+    for n in ("ds_w1", "ds_w2"):
+        if dl.g[n] is None:
+            continue
+        g_all = dl.g[n].float().cpu().numpy().reshape(L.E, -1)
+        assert np.all(np.isfinite(g_all)), f"{n}: non-finite values"
+        missing = [e for e in range(L.E) if counts[e] > 0 and not np.any(g_all[e] != 0)]
+        assert not missing, f"{n}: experts with rows but no gradient: {missing[:10]}"
+
     # F7, B7 and d topk_w on sampled tokens, from the device's own Y_r and dX^
     toks = np.unique(np.concatenate([[0, L.T - 1], rng.choice(L.T, size=64, replace=False)]))
     rsel = row_of.reshape(L.T, k)[toks]
