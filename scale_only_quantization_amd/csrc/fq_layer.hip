@@ -822,17 +822,17 @@ __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
             for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
         const Slots sl = load_slots(a.ids, a.row_of, nullptr, t, a.k, a.E, a.T * a.k, lane);
         float rp = 0.0f;
-        for (int j = 0; j < a.k; ++j) {
+        // copy j's part of the routed gradient, reduced into acc; dv: its
+        // vectors, already loaded
+        auto reduce_copy = [&](int j, const uint4* dv) {
             const int e = slot_i(sl.e, j);
-            const int64_t row = slot_i(sl.row, j);
-            const uint4* src = reinterpret_cast<const uint4*>(a.dxh + row * a.H + hf * nvl * 8);
             float part_row = 0.0f;
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
                 const int v = lane + c * WAVE;
                 if (v >= nvec) continue;
                 float d[8];
-                unpack8(src[v], d);
+                unpack8(dv[c], d);
                 if (recompute) {
                     float f[8], gx[8], dfac;
                     unpack8(xv[c], f);
@@ -849,6 +849,36 @@ __global__ __launch_bounds__(TPB) void k_unpermute_a1(UnpermuteArgs a) {
             if (a.rowpart) {
                 const float tot = wave_sum(part_row);
                 rp = lane == j ? tot : rp;
+            }
+        };
+        auto copy_src = [&](int j) {
+            return reinterpret_cast<const uint4*>(a.dxh + (int64_t)slot_i(sl.row, j) * a.H + hf * nvl * 8);
+        };
+        bool done = false;
+        if constexpr (NV == 1) {
+            if (a.k == KU && nvec == WAVE) {
+                // straight-line top-KU: copy j+1's load goes out before copy j
+                // is reduced, so each wait names one load (no stores between)
+                uint4 db[2][1];
+                db[0][0] = copy_src(0)[lane];
+#pragma unroll
+                for (int j = 0; j < KU; ++j) {
+                    if (j + 1 < KU) db[(j + 1) & 1][0] = copy_src(j + 1)[lane];
+                    reduce_copy(j, db[j & 1]);
+                }
+                done = true;
+            }
+        }
+        if (!done) {
+            for (int j = 0; j < a.k; ++j) {
+                const uint4* src = copy_src(j);
+                uint4 dv[NV];
+#pragma unroll
+                for (int c = 0; c < NV; ++c) {
+                    const int v = lane + c * WAVE;
+                    dv[c] = v < nvec ? src[v] : make_uint4(0, 0, 0, 0);
+                }
+                reduce_copy(j, dv);
             }
         }
         // lane j holds copy j's row and partial: one store after the loop, so
