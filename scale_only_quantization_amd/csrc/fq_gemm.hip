@@ -863,7 +863,9 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         // Persistent: the blocks of XCD group x = blockIdx % 8 (dealt to XCD x)
         // take the tiles of that XCD's experts (longest first) from a counter,
         // so the tiles sharing an expert's operand rows meet in one L2.  The
-        // next tile's first loads are issued before this tile's epilogue.
+        // next tile's first loads are issued during this tile's epilogue (with
+        // the fused scale gradient: once its first weights and scales have
+        // landed; without it: before it).
         // Slots are taken one tile ahead: tile t's epilogue takes the slot of
         // tile t + 2 into s_q[t & 1], read after tile t + 1's main loop (main
         // loop barriers separate each write from the reads around it), so the
@@ -895,8 +897,8 @@ __global__ __launch_bounds__(64 * WVM * WVN) __attribute__((amdgpu_waves_per_eu(
         __syncthreads();
         const int slot = __builtin_amdgcn_readfirstlane(s_slot);
         if (slot < 0 || slot >= tiles_x) return;
-        // The next tile's first PRE steps are issued before this tile's
-        // epilogue, into stages [0, PRE); the fused epilogue's weights go
+        // The next tile's first PRE steps go into stages [0, PRE) during this
+        // tile's epilogue; the fused epilogue's weights go
         // through the stages after them (of A for waves 0-3, of B for waves
         // 4-7), two 4-KB slots per wave.
         // (without that epilogue the whole prologue, S-1 steps)
