@@ -24,11 +24,14 @@ enum Source : int { S_LEARNABLE = 0, S_STATIC = 1, S_DYNAMIC = 2 };
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+// Two fp32 -> packed bf16 pair (a in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32 with both operands (two scalar casts become two
+// conversions, a shift and an or).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    __bf16 ha = (__bf16)a, hb = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {

@@ -8,6 +8,8 @@
 //             A = sum e^{zt - mt} (zt - zs)   -> kl  = A / St + lse_s - lse_t
 //             B = sum e^{zs - ms} (zs - zt)   -> rkl = B / Ss + lse_t - lse_s
 //           the teacher's confidence is 1 / St (its largest probability);
+//           the sums run in base 2 (the frame m log2 e, one fused
+//           multiply-add per exponent);
 //           a fixed tree combines the threads' partial states.
 //   pass 2  d loss / d zs per element (q = e^{zs - lse_s}, p = e^{zt - lse_t}):
 //             kl  q - p;  rkl  q ((zs - lse_s) - (zt - lse_t) - rkl);
@@ -33,13 +35,23 @@ __device__ __forceinline__ int clamp_id(int v, int n) { return v < 0 ? 0 : (v >=
 __device__ __forceinline__ float bf_from_bits(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-struct OnlineSum {          // running max m, sum of e^{x - m}, and a weighted sum in the same frame
+constexpr float LOG2E = 0x1.715476p+0f;   // log2(e) and ln(2), rounded to fp32
+constexpr float LN2 = 0x1.62e430p-1f;
+// 2^x with the hardware exponential (a few ulp; results below the normal
+// range may flush to zero, which the sums here cannot notice)
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Running sums in base 2: the frame m is fl(max x * log2 e), s = sum of
+// 2^{x log2 e - m} (each exponent one fused multiply-add), and a weighted sum
+// in the same frame.  Ratios of the sums do not depend on the frame; the log
+// of the sum of e^x is m ln 2 + ln s.
+struct OnlineSum {
     float m = -INFINITY, s = 0.0f, a = 0.0f;
     __device__ __forceinline__ void merge(float m2, float s2, float a2) {
         const float mm = fmaxf(m, m2);
         if (mm == -INFINITY) return;
-        const float f1 = m == -INFINITY ? 0.0f : __expf(m - mm);
-        const float f2 = m2 == -INFINITY ? 0.0f : __expf(m2 - mm);
+        const float f1 = m == -INFINITY ? 0.0f : exp2_hw(m - mm);
+        const float f2 = m2 == -INFINITY ? 0.0f : exp2_hw(m2 - mm);
         s = s * f1 + s2 * f2;
         a = a * f1 + a2 * f2;
         m = mm;
@@ -85,7 +97,7 @@ __global__ __launch_bounds__(DTPB) void k_distill(DistillArgs a) {
         // ---- pass 1
         OnlineSum st_, ss_;              // teacher (with A), student (with B)
         for (int v = threadIdx.x; v < nvec; v += DTPB) {
-            float fs[8], ft[8];
+            float fs[8], ft[8], dts[8];      // dts = zt - zs
             unpack8(zs[v], fs);
             float mv = fs[0];
 #pragma unroll
@@ -96,37 +108,40 @@ __global__ __launch_bounds__(DTPB) void k_distill(DistillArgs a) {
                 float mt = ft[0];
 #pragma unroll
                 for (int i = 1; i < 8; ++i) mt = fmaxf(mt, ft[i]);
+                mt *= LOG2E;
                 if (mt > st_.m) {
-                    const float f = __expf(st_.m - mt);
+                    const float f = exp2_hw(st_.m - mt);
                     st_.s *= f;
                     st_.a *= f;
                     st_.m = mt;
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float e = __expf(ft[i] - st_.m);
+                    const float e = exp2_hw(__builtin_fmaf(ft[i], LOG2E, -st_.m));
                     st_.s += e;
-                    st_.a += e * (ft[i] - fs[i]);
+                    dts[i] = ft[i] - fs[i];
+                    st_.a = __builtin_fmaf(e, dts[i], st_.a);
                 }
             }
+            mv *= LOG2E;
             if (mv > ss_.m) {
-                const float f = __expf(ss_.m - mv);
+                const float f = exp2_hw(ss_.m - mv);
                 ss_.s *= f;
                 ss_.a *= f;
                 ss_.m = mv;
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float e = __expf(fs[i] - ss_.m);
+                const float e = exp2_hw(__builtin_fmaf(fs[i], LOG2E, -ss_.m));
                 ss_.s += e;
-                if (KIND == DK_RKL || KIND == DK_CAKLD) ss_.a += e * (fs[i] - ft[i]);
+                if (KIND == DK_RKL || KIND == DK_CAKLD) ss_.a = __builtin_fmaf(-e, dts[i], ss_.a);
             }
         }
         block_merge(st_, ss_, red);
-        const float lse_s = ss_.m + __logf(ss_.s);
+        const float lse_s = __builtin_fmaf(ss_.m, LN2, __logf(ss_.s));
         float lse_t = 0.0f, kl = 0.0f, rkl = 0.0f, conf = 1.0f;
         if (KIND != DK_TOPK) {
-            lse_t = st_.m + __logf(st_.s);
+            lse_t = __builtin_fmaf(st_.m, LN2, __logf(st_.s));
             kl = st_.a / st_.s + lse_s - lse_t;
             rkl = ss_.a / ss_.s + lse_t - lse_s;
             conf = 1.0f / st_.s;
@@ -162,22 +177,32 @@ __global__ __launch_bounds__(DTPB) void k_distill(DistillArgs a) {
         // ---- pass 2
         uint4* g = reinterpret_cast<uint4*>(a.grad + r * a.V);
         const float ws = a.inv_T * (a.labels ? a.lm_w : 0.0f), wd = a.inv_T * a.dist_w;
+        // ws q + wd gk per kind, gathered in q and p with the row's constants
+        // (d = (zs - zt) - (lse_s - lse_t + rkl) is the rkl-term's factor):
+        //   kl     q (ws + wd) - wd p          rkl    q (ws + wd d)
+        //   cakld  q (ws + wd c + wd (1 - c) d) - wd c p
+        //   top-k  q (ws + wd)  (the k ids are rewritten below)
+        const float lsL = lse_s * LOG2E, ltL = lse_t * LOG2E;
+        const float c0 = (lse_s - lse_t) + rkl;
+        const float k1 = KIND == DK_RKL ? ws : KIND == DK_CAKLD ? ws + wd * conf : ws + wd;
+        const float k2 = KIND == DK_RKL ? wd : wd * (1.0f - conf);
+        const float k3 = KIND == DK_KL ? wd : wd * conf;
         for (int v = threadIdx.x; v < nvec; v += DTPB) {
             float fs[8], ft[8], o[8];
             unpack8(zs[v], fs);
             if (KIND != DK_TOPK) unpack8(zt[v], ft);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float lq = fs[i] - lse_s;
-                const float q = __expf(lq);
-                float gk = q;
-                if (KIND != DK_TOPK) {
-                    const float lp = ft[i] - lse_t;
-                    const float p = __expf(lp);
-                    const float gr = q * ((lq - lp) - rkl);
-                    gk = KIND == DK_KL ? q - p : KIND == DK_RKL ? gr : conf * (q - p) + (1.0f - conf) * gr;
+                const float q = exp2_hw(__builtin_fmaf(fs[i], LOG2E, -lsL));
+                if (KIND == DK_TOPK) {
+                    o[i] = q * k1;
+                } else {
+                    const float p = exp2_hw(__builtin_fmaf(ft[i], LOG2E, -ltL));
+                    const float d = (fs[i] - ft[i]) - c0;
+                    if (KIND == DK_KL) o[i] = __builtin_fmaf(q, k1, -k3 * p);
+                    else if (KIND == DK_RKL) o[i] = q * __builtin_fmaf(k2, d, k1);
+                    else o[i] = __builtin_fmaf(q, __builtin_fmaf(k2, d, k1), -k3 * p);
                 }
-                o[i] = ws * q + wd * gk;
             }
             g[v] = pack8(o);
         }
