@@ -86,6 +86,24 @@ __device__ __forceinline__ void block_merge(OnlineSum& o1, OnlineSum& o2, float*
     o2 = r2;
 }
 
+// DU vectors of 8 logits per thread in flight: the row's vectors v0,
+// v0 + DTPB, ... (zero past the row's end) of the student and, with TEACHER,
+// the teacher
+constexpr int DU = 4;
+template <bool TEACHER>
+__device__ __forceinline__ void load_vecs(const uint4* zs, const uint4* zt, int v0, int nvec, uint4* bs,
+                                          uint4* bt) {
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+        const int v = v0 + u * DTPB;
+        bs[u] = bt[u] = make_uint4(0, 0, 0, 0);
+        if (v < nvec) {
+            bs[u] = zs[v];
+            if (TEACHER) bt[u] = zt[v];
+        }
+    }
+}
+
 template <int KIND>
 __global__ __launch_bounds__(DTPB) void k_distill(DistillArgs a) {
     __shared__ float red[DWAVES * 6];
@@ -96,45 +114,54 @@ __global__ __launch_bounds__(DTPB) void k_distill(DistillArgs a) {
         const uint4* zt = reinterpret_cast<const uint4*>(a.zt + r * a.V);
         // ---- pass 1
         OnlineSum st_, ss_;              // teacher (with A), student (with B)
-        for (int v = threadIdx.x; v < nvec; v += DTPB) {
-            float fs[8], ft[8], dts[8];      // dts = zt - zs
-            unpack8(zs[v], fs);
-            float mv = fs[0];
+        // DU vectors' loads per thread go out before any is summed; they are
+        // taken in the order of one at a time (v, v + DTPB, ...), so the sums
+        // are the same
+        for (int v0 = threadIdx.x; v0 < nvec; v0 += DU * DTPB) {
+            uint4 bs[DU], bt[DU];
+            load_vecs<KIND != DK_TOPK>(zs, zt, v0, nvec, bs, bt);
 #pragma unroll
-            for (int i = 1; i < 8; ++i) mv = fmaxf(mv, fs[i]);
-            // running sums rescaled only when the vector raises the running max
-            if (KIND != DK_TOPK) {
-                unpack8(zt[v], ft);
-                float mt = ft[0];
+            for (int u = 0; u < DU; ++u) {
+                if (v0 + u * DTPB >= nvec) break;
+                float fs[8], ft[8], dts[8];      // dts = zt - zs
+                unpack8(bs[u], fs);
+                float mv = fs[0];
 #pragma unroll
-                for (int i = 1; i < 8; ++i) mt = fmaxf(mt, ft[i]);
-                mt *= LOG2E;
-                if (mt > st_.m) {
-                    const float f = exp2_hw(st_.m - mt);
-                    st_.s *= f;
-                    st_.a *= f;
-                    st_.m = mt;
+                for (int i = 1; i < 8; ++i) mv = fmaxf(mv, fs[i]);
+                // running sums rescaled only when the vector raises the running max
+                if (KIND != DK_TOPK) {
+                    unpack8(bt[u], ft);
+                    float mt = ft[0];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, ft[i]);
+                    mt *= LOG2E;
+                    if (mt > st_.m) {
+                        const float f = exp2_hw(st_.m - mt);
+                        st_.s *= f;
+                        st_.a *= f;
+                        st_.m = mt;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float e = exp2_hw(__builtin_fmaf(ft[i], LOG2E, -st_.m));
+                        st_.s += e;
+                        dts[i] = ft[i] - fs[i];
+                        st_.a = __builtin_fmaf(e, dts[i], st_.a);
+                    }
+                }
+                mv *= LOG2E;
+                if (mv > ss_.m) {
+                    const float f = exp2_hw(ss_.m - mv);
+                    ss_.s *= f;
+                    ss_.a *= f;
+                    ss_.m = mv;
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float e = exp2_hw(__builtin_fmaf(ft[i], LOG2E, -st_.m));
-                    st_.s += e;
-                    dts[i] = ft[i] - fs[i];
-                    st_.a = __builtin_fmaf(e, dts[i], st_.a);
+                    const float e = exp2_hw(__builtin_fmaf(fs[i], LOG2E, -ss_.m));
+                    ss_.s += e;
+                    if (KIND == DK_RKL || KIND == DK_CAKLD) ss_.a = __builtin_fmaf(-e, dts[i], ss_.a);
                 }
-            }
-            mv *= LOG2E;
-            if (mv > ss_.m) {
-                const float f = exp2_hw(ss_.m - mv);
-                ss_.s *= f;
-                ss_.a *= f;
-                ss_.m = mv;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float e = exp2_hw(__builtin_fmaf(fs[i], LOG2E, -ss_.m));
-                ss_.s += e;
-                if (KIND == DK_RKL || KIND == DK_CAKLD) ss_.a = __builtin_fmaf(-e, dts[i], ss_.a);
             }
         }
         block_merge(st_, ss_, red);
@@ -187,24 +214,30 @@ __global__ __launch_bounds__(DTPB) void k_distill(DistillArgs a) {
         const float k1 = KIND == DK_RKL ? ws : KIND == DK_CAKLD ? ws + wd * conf : ws + wd;
         const float k2 = KIND == DK_RKL ? wd : wd * (1.0f - conf);
         const float k3 = KIND == DK_KL ? wd : wd * conf;
-        for (int v = threadIdx.x; v < nvec; v += DTPB) {
-            float fs[8], ft[8], o[8];
-            unpack8(zs[v], fs);
-            if (KIND != DK_TOPK) unpack8(zt[v], ft);
+        for (int v0 = threadIdx.x; v0 < nvec; v0 += DU * DTPB) {
+            uint4 bs[DU], bt[DU];
+            load_vecs<KIND != DK_TOPK>(zs, zt, v0, nvec, bs, bt);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float q = exp2_hw(__builtin_fmaf(fs[i], LOG2E, -lsL));
-                if (KIND == DK_TOPK) {
-                    o[i] = q * k1;
-                } else {
-                    const float p = exp2_hw(__builtin_fmaf(ft[i], LOG2E, -ltL));
-                    const float d = (fs[i] - ft[i]) - c0;
-                    if (KIND == DK_KL) o[i] = __builtin_fmaf(q, k1, -k3 * p);
-                    else if (KIND == DK_RKL) o[i] = q * __builtin_fmaf(k2, d, k1);
-                    else o[i] = __builtin_fmaf(q, __builtin_fmaf(k2, d, k1), -k3 * p);
+            for (int u = 0; u < DU; ++u) {
+                if (v0 + u * DTPB >= nvec) break;
+                float fs[8], ft[8], o[8];
+                unpack8(bs[u], fs);
+                if (KIND != DK_TOPK) unpack8(bt[u], ft);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float q = exp2_hw(__builtin_fmaf(fs[i], LOG2E, -lsL));
+                    if (KIND == DK_TOPK) {
+                        o[i] = q * k1;
+                    } else {
+                        const float p = exp2_hw(__builtin_fmaf(ft[i], LOG2E, -ltL));
+                        const float d = (fs[i] - ft[i]) - c0;
+                        if (KIND == DK_KL) o[i] = __builtin_fmaf(q, k1, -k3 * p);
+                        else if (KIND == DK_RKL) o[i] = q * __builtin_fmaf(k2, d, k1);
+                        else o[i] = __builtin_fmaf(q, __builtin_fmaf(k2, d, k1), -k3 * p);
+                    }
                 }
+                g[v0 + u * DTPB] = pack8(o);
             }
-            g[v] = pack8(o);
         }
         __syncthreads();                 // every element written before the special ones are rewritten
         if (threadIdx.x < WAVE) {
