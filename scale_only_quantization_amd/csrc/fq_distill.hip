@@ -41,6 +41,12 @@ constexpr float LN2 = 0x1.62e430p-1f;
 // range may flush to zero, which the sums here cannot notice)
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Keeps the block it stands in behind a branch: the compiler would otherwise
+// evaluate a short conditional block (a rescale: one exponential, two
+// products) on every pass and select, where a skipped branch costs a few
+// scalar instructions once no lane's maximum rises any more.
+__device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
+
 // Running sums in base 2: the frame m is fl(max x * log2 e), s = sum of
 // 2^{x log2 e - m} (each exponent one fused multiply-add), and a weighted sum
 // in the same frame.  Ratios of the sums do not depend on the frame; the log
@@ -136,6 +142,7 @@ __global__ __launch_bounds__(DTPB) void k_distill(DistillArgs a) {
                     for (int i = 1; i < 8; ++i) mt = fmaxf(mt, ft[i]);
                     mt *= LOG2E;
                     if (mt > st_.m) {
+                        keep_branch();
                         const float f = exp2_hw(st_.m - mt);
                         st_.s *= f;
                         st_.a *= f;
@@ -151,6 +158,7 @@ __global__ __launch_bounds__(DTPB) void k_distill(DistillArgs a) {
                 }
                 mv *= LOG2E;
                 if (mv > ss_.m) {
+                    keep_branch();
                     const float f = exp2_hw(ss_.m - mv);
                     ss_.s *= f;
                     ss_.a *= f;
