@@ -18,7 +18,9 @@
 //           The label and the top-k ids are rewritten after a barrier by one
 //           wave, from the inputs, so each element is rounded once.
 // Per row: 4 B (kl/rkl/cakld: 2 x bf16 logits) read per element per pass and
-// 2 B written; HBM bound.
+// 2 B written.  With the teacher's logits the four exponentials per element
+// keep the kernel near the vector issue rate; top-k (one input) is bound by
+// its loads, so each thread keeps DU vectors' loads in flight.
 #include <hip/hip_runtime.h>
 
 #include "fq_common.h"
